@@ -1,0 +1,274 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * What the library does.  A sequence's KV cache lives in fixed-size physical
+ * blocks of B tokens; a per-sequence block table maps logical block i // B to
+ * a physical block id ("Paged Attention" (daiw.org), 直觉 and 定义).  The host
+ * block pool hands blocks out and takes them back, shares them between
+ * sequences by reference count and copies a still-shared last block before a
+ * sequence writes into it ("vllm-pagedattention" (chenyuan1125.github.io),
+ * 页表真正解开的… and 一块内存，如何安全地属于多条序列).  Three device
+ * operations serve one decode step: pa_copy_blocks (those copies),
+ * pa_write_kv (the new token's K/V into its slot) and pa_decode
+ * (single-query attention whose K/V rows are found through the tables).
+ * pa_decode_contiguous computes the same attention on the contiguous
+ * one-region-per-sequence layout the pages compare paging against.
+ *
+ * Conventions shared by every call
+ * - Status: every call returns a pa_status; PA_OK is 0, errors are negative.
+ *   No C++ exception and no abort crosses this boundary.  pa_last_error()
+ *   gives a human-readable detail of the calling thread's last failure.
+ * - Device memory: every device pointer is owned by the caller (for instance
+ *   a torch tensor's data_ptr()).  The library never allocates, frees or
+ *   synchronises device memory; device calls only enqueue work on the given
+ *   stream (a hipStream_t passed as pa_stream; NULL = the null stream) and
+ *   return once it is enqueued.
+ * - Host memory: the pool owns its host state until pa_pool_destroy.  Output
+ *   arrays are caller-owned and written only on PA_OK unless a call says
+ *   otherwise.
+ * - Shapes are checked on the host before anything is enqueued: a bad
+ *   argument gives PA_E_INVAL, a shape or dtype outside the supported set
+ *   gives PA_E_UNSUPPORTED; neither launches anything.
+ * - Threading: a pool is not thread-safe (callers serialise calls on one
+ *   pool); device calls are reentrant.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_E_INVAL (-1)        /* bad argument (null pointer, negative size, ...) */
+#define PA_E_NOBLOCKS (-2)     /* pool exhausted: the request is refused, nothing changed */
+#define PA_E_NOSEQ (-3)        /* unknown sequence id */
+#define PA_E_EXISTS (-4)       /* sequence id already in use */
+#define PA_E_UNSUPPORTED (-5)  /* shape / dtype outside the compiled set */
+#define PA_E_HIP (-6)          /* the HIP runtime refused a launch */
+
+typedef int32_t pa_dtype;
+#define PA_F32 0
+#define PA_F16 1
+#define PA_BF16 2
+
+typedef void* pa_stream; /* a hipStream_t */
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* pa_strerror(pa_status status);
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* pa_last_error(void);
+/* Library ABI version, currently 1. */
+int32_t pa_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* Host block pool                                                            */
+/* ------------------------------------------------------------------------- */
+/*
+ * Rules ("vLLM PagedAttention：大模型推理的显存管理革命" (horeb.top), 分配策略
+ * and 内存共享：写时复制; "vllm-paged-attention-engine" (aiqz.cc), 分页存储设计
+ * and the allocator of Python 演示; "vllm-pagedattention", 一块内存…):
+ * - a sequence of n tokens holds ceil(n / B) blocks;
+ * - free blocks are taken from the front of the free list and released blocks
+ *   are appended at its back, in table order;
+ * - a token goes into the last block while it has room; a full last block
+ *   makes the pool append one more block to the table;
+ * - fork shares every block of the parent (reference count + 1 each);
+ * - writing into a last block whose count is > 1 first copies it: the
+ *   sequence's last entry is remapped to a fresh block (taken from the front)
+ *   and the caller must copy src -> dst on the device (pa_copy_blocks)
+ *   before writing the token; full blocks are never copied;
+ * - a block returns to the free list when its count reaches 0;
+ * - a request the pool cannot cover is refused with PA_E_NOBLOCKS and leaves
+ *   the pool unchanged ("Paged Attention", 读者问答 / 运维提示: an exhausted
+ *   pool rejects requests rather than failing).
+ * The slot of logical token i of a sequence is table[i / B] * B + i % B; it
+ * indexes the device caches' [num_blocks * B] token rows (see pa_write_kv).
+ */
+typedef struct pa_pool pa_pool;
+
+typedef struct pa_pool_stats_t {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t free_blocks;    /* blocks on the free list */
+  int32_t used_blocks;    /* blocks with reference count >= 1 */
+  int32_t shared_blocks;  /* blocks with reference count >= 2 */
+  int32_t num_seqs;
+  int64_t tokens;         /* sum of sequence lengths */
+  int64_t waste_tokens;   /* sum over sequences of empty slots in their tables
+                             (each < B; "Paged Attention", 定义: waste is
+                             confined to the last block) */
+} pa_pool_stats_t;
+
+/* Create a pool of num_blocks blocks of block_size tokens (both > 0 and
+ * num_blocks < 2^31 / block_size).  initial_free_order: NULL for 0..n-1, else
+ * a permutation of 0..n-1 (PA_E_INVAL otherwise), copied. */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* initial_free_order, pa_pool** out);
+void pa_pool_destroy(pa_pool* pool); /* NULL is a no-op */
+
+/* Admit seq with n_tokens >= 0 prompt tokens, taking ceil(n/B) blocks at
+ * once.  slots_out (nullable) receives the n_tokens slots.  PA_E_EXISTS if seq
+ * is live, PA_E_NOBLOCKS if the pool is short (nothing taken). */
+pa_status pa_seq_alloc(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out);
+
+/* Grow seq by one token and return its slot.  If the token lands in a
+ * still-shared last block, *cow_src / *cow_dst receive the block pair the
+ * caller must copy on the device first; otherwise both are -1.  Output
+ * pointers are nullable. */
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int64_t* slot_out,
+                        int32_t* cow_src, int32_t* cow_dst);
+
+/* n >= 0 successive pa_seq_append calls as one all-or-nothing request:
+ * slots_out (nullable, n entries); at most the first token can need a copy,
+ * reported as in pa_seq_append. */
+pa_status pa_seq_extend(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_out,
+                        int32_t* cow_src, int32_t* cow_dst);
+
+/* child shares all of parent's blocks and its length.  PA_E_NOSEQ if parent
+ * is unknown, PA_E_EXISTS if child is live (including child == parent). */
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child);
+
+/* Release seq: reference counts drop in table order; blocks reaching 0 go to
+ * the back of the free list. */
+pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+
+pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len_out);
+
+/* Block tables of n sequences as an n x max_blocks int32 row-major array,
+ * padded with -1, and their lengths (ctx_out, nullable).  PA_E_NOSEQ for an
+ * unknown id, PA_E_INVAL when a table is wider than max_blocks; on error the
+ * output arrays hold unspecified values. */
+pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t n,
+                               int32_t max_blocks, int32_t* tables_out, int32_t* ctx_out);
+
+pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
+/* Reference count of a block, or -1 for an id outside [0, num_blocks). */
+int32_t pa_pool_refcount(const pa_pool* pool, int32_t block);
+/* Free list front to back into out[0 .. min(cap, free)-1]; *n_out = free count. */
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* ------------------------------------------------------------------------- */
+/* Device operations                                                          */
+/* ------------------------------------------------------------------------- */
+/*
+ * Cache layout (both K and V): [num_blocks][num_kv_heads][block_size][head_dim],
+ * dense, row-major, elements of the cache dtype.  One (block, kv head) tile
+ * of block_size * head_dim elements is contiguous, so a block is contiguous
+ * inside and blocks sit anywhere ("Paged Attention", 定义).
+ * Supported set: head_dim in {64, 128}; block_size in {8, 16, 32};
+ * dtype in {PA_F32, PA_F16, PA_BF16}.
+ */
+
+/* Scatter num_tokens new tokens into their slots ("vllm-pagedattention",
+ * 页表真正解开的…: a new token is written into the last block while it has
+ * room).  k_new, v_new: [num_tokens][num_kv_heads][head_dim] device arrays;
+ * slot_mapping: num_tokens int64 device array; token t goes to block
+ * slot / B, row slot % B.  A negative slot is padding and is skipped; a slot
+ * >= num_blocks * B is skipped as well (never written out of bounds).  Bit
+ * copy: no arithmetic on the values.  Slots must be distinct (duplicates
+ * race). */
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      pa_dtype dtype, pa_stream stream);
+
+/* Copy-on-write block copies ("vllm-pagedattention", 一块内存…: the shared last
+ * block is copied before the branch writes).  pairs: n_pairs x 2 int32 device
+ * array of (src, dst); each copies the whole block, every KV head, in K and in
+ * V.  Pairs whose ids fall outside [0, num_blocks) are skipped.  Pairs run
+ * concurrently: no block may be both a source and a destination in one call. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, pa_dtype dtype, pa_stream stream);
+
+/*
+ * Decode attention, one query token per sequence.  For sequence s and query
+ * head h (KV head g = h / (Hq / Hkv), consecutive grouping):
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) * V_t,  t in [0, ctx_lens[s]),
+ * with token t's rows in block block_tables[s][t / B], row t % B
+ * ("Paged Attention", 直觉; "vllm-pagedattention", 页表真正解开的…: the kernel
+ * fetches each block through the table and does scores, softmax and the
+ * weighted sum of V; the attention itself is unchanged).  The new token must
+ * have been written already (it attends to itself).
+ *
+ * Contexts longer than partition_size are cut into partitions that are
+ * reduced independently and merged with the log-sum-exp identity (needs the
+ * workspace).  Arithmetic is float32 (16-bit inputs are widened exactly);
+ * results do not depend on which physical blocks hold the tokens, and are
+ * bitwise reproducible for a given (shape, partition_size).
+ */
+typedef struct pa_decode_args {
+  void* out;                   /* [S][Hq][head_dim], out_dtype */
+  pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
+  const void* q;               /* [S][Hq][head_dim], kv_dtype */
+  const void* k_cache;         /* layout above, kv_dtype */
+  const void* v_cache;
+  pa_dtype kv_dtype;
+  const int32_t* block_tables; /* [S][max_blocks] device; entries j < ceil(ctx/B) are read */
+  const int32_t* ctx_lens;     /* [S] device */
+  int32_t num_seqs;            /* S >= 0 (0: nothing to do) */
+  int32_t num_q_heads;         /* Hq, a multiple of Hkv with Hq / Hkv in {1, 2, 4, 8} */
+  int32_t num_kv_heads;        /* Hkv > 0 */
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks;          /* table row width > 0 */
+  int32_t num_blocks;          /* physical blocks in the caches */
+  int32_t max_ctx;             /* 0 or an upper bound on ctx_lens; sizes the grid
+                                  (0 means max_blocks * block_size) */
+  float scale;                 /* finite, e.g. 1/sqrt(head_dim) */
+  int32_t partition_size;      /* 0 = automatic; else a multiple of 8 and of
+                                  block_size, at most min(512, 64 * block_size) */
+  void* workspace;             /* device scratch, >= pa_decode_workspace_bytes */
+  size_t workspace_bytes;
+} pa_decode_args;
+/*
+ * Device-side data: a ctx_lens entry <= 0 yields a zero output row; entries
+ * above max_ctx are clamped to it (the caller guarantees they do not occur);
+ * table entries are clamped into [0, num_blocks) so that a corrupt table can
+ * never read outside the caches (its sequence's output is then meaningless).
+ */
+
+/* Workspace bytes pa_decode needs for these arguments (0 when every context
+ * fits one partition).  Validates the arguments like pa_decode. */
+pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_out);
+pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
+
+/*
+ * The same attention on the contiguous layout the pages contrast paging with
+ * ("Paged Attention", 定义: one region per sequence reserved for its maximum
+ * length): K and V are [S][Hkv][capacity][head_dim]; no block table.  Used to
+ * measure what the table indirection costs.
+ */
+typedef struct pa_contig_args {
+  void* out;
+  pa_dtype out_dtype;
+  const void* q;
+  const void* k;               /* [S][Hkv][capacity][head_dim] */
+  const void* v;
+  pa_dtype kv_dtype;
+  const int32_t* ctx_lens;     /* [S] device, each <= capacity */
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;            /* token rows reserved per (sequence, KV head) */
+  int32_t max_ctx;             /* 0 or an upper bound on ctx_lens (0 = capacity) */
+  float scale;
+  int32_t partition_size;      /* 0 = automatic; multiple of 8, at most 512 */
+  void* workspace;
+  size_t workspace_bytes;
+} pa_contig_args;
+
+pa_status pa_decode_contiguous_workspace_bytes(const pa_contig_args* args, size_t* bytes_out);
+pa_status pa_decode_contiguous(const pa_contig_args* args, pa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

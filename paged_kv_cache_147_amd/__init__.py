@@ -1,0 +1,9 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+The compute path lives in ``libpagedkv.so`` (C ABI: include/pagedkv.h); this
+package is its Python binding.  Build the library with
+``python -m paged_kv_cache_147_amd.build``.
+"""
+from ._lib import (EXPORTED, PA_BF16, PA_F16, PA_F32, BlockPool, PagedKVError,  # noqa: F401
+                   current_stream, pa_copy_blocks, pa_decode, pa_decode_contiguous,
+                   pa_decode_workspace_bytes, pa_write_kv, raw)

@@ -1,0 +1,356 @@
+"""ctypes binding of libpagedkv.so: argument marshalling only.
+
+Every function named ``pa_*`` here calls the C entry point of the same name
+(include/pagedkv.h); the tensor helpers only turn torch tensors into device
+pointers and torch's current stream into a hipStream_t.  Nothing in this
+module computes any part of the decode path, and nothing falls back to a CPU
+implementation: if the library is missing, importing it raises.
+"""
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PA_OK, PA_E_INVAL, PA_E_NOBLOCKS, PA_E_NOSEQ, PA_E_EXISTS, PA_E_UNSUPPORTED, PA_E_HIP = 0, -1, -2, -3, -4, -5, -6
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+STATUS_NAMES = {0: "OK", -1: "INVAL", -2: "NOBLOCKS", -3: "NOSEQ", -4: "EXISTS", -5: "UNSUPPORTED",
+                -6: "HIP"}
+TORCH_DTYPE = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
+DTYPE_OF = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+NAME_OF = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status, func):
+        self.status = status
+        self.code = STATUS_NAMES.get(status, str(status))
+        detail = _lib.pa_last_error().decode() if _lib is not None else ""
+        super().__init__(f"{func}: {self.code} ({detail})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_147_amd.build` "
+            "(the decode path has no fallback)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = None
+_lib = _load()
+
+c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+P_i32, P_i64 = ctypes.POINTER(c_i32), ctypes.POINTER(c_i64)
+
+
+class pa_pool_stats_t(ctypes.Structure):
+    _fields_ = [("num_blocks", c_i32), ("block_size", c_i32), ("free_blocks", c_i32),
+                ("used_blocks", c_i32), ("shared_blocks", c_i32), ("num_seqs", c_i32),
+                ("tokens", c_i64), ("waste_tokens", c_i64)]
+
+
+class pa_decode_args(ctypes.Structure):
+    _fields_ = [("out", c_vp), ("out_dtype", c_i32), ("q", c_vp), ("k_cache", c_vp),
+                ("v_cache", c_vp), ("kv_dtype", c_i32), ("block_tables", c_vp), ("ctx_lens", c_vp),
+                ("num_seqs", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
+                ("head_dim", c_i32), ("block_size", c_i32), ("max_blocks", c_i32),
+                ("num_blocks", c_i32), ("max_ctx", c_i32), ("scale", c_f32),
+                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class pa_contig_args(ctypes.Structure):
+    _fields_ = [("out", c_vp), ("out_dtype", c_i32), ("q", c_vp), ("k", c_vp), ("v", c_vp),
+                ("kv_dtype", c_i32), ("ctx_lens", c_vp), ("num_seqs", c_i32),
+                ("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
+                ("capacity", c_i32), ("max_ctx", c_i32), ("scale", c_f32),
+                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+_SIGS = {
+    "pa_strerror": (ctypes.c_char_p, [c_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (c_i32, []),
+    "pa_pool_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
+    "pa_pool_destroy": (None, [c_vp]),
+    "pa_seq_alloc": (c_i32, [c_vp, c_i64, c_i32, P_i64]),
+    "pa_seq_append": (c_i32, [c_vp, c_i64, P_i64, P_i32, P_i32]),
+    "pa_seq_extend": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
+    "pa_seq_fork": (c_i32, [c_vp, c_i64, c_i64]),
+    "pa_seq_free": (c_i32, [c_vp, c_i64]),
+    "pa_seq_len": (c_i32, [c_vp, c_i64, P_i32]),
+    "pa_pool_block_tables": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
+    "pa_pool_stats": (c_i32, [c_vp, ctypes.POINTER(pa_pool_stats_t)]),
+    "pa_pool_refcount": (c_i32, [c_vp, c_i32]),
+    "pa_pool_free_list": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
+    "pa_write_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_decode_workspace_bytes": (c_i32, [ctypes.POINTER(pa_decode_args), ctypes.POINTER(c_sz)]),
+    "pa_decode": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
+    "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
+    "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
+}
+EXPORTED = tuple(_SIGS)
+
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def raw():
+    """The ctypes library object (every pa_* symbol with its signature)."""
+    return _lib
+
+
+def check(status, func):
+    if status != PA_OK:
+        raise PagedKVError(status, func)
+    return status
+
+
+def _ptr(arr, ctype):
+    """Host numpy array -> ctypes pointer (None for None)."""
+    if arr is None:
+        return None
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def current_stream(device=None):
+    """torch's current stream on ``device`` as a raw hipStream_t."""
+    return c_vp(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return c_vp(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Host pool
+# ---------------------------------------------------------------------------
+
+class BlockPool:
+    """Owner of a native pa_pool handle; each method is one pa_* call."""
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None):
+        import numpy as np
+        handle = c_vp()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+        check(_lib.pa_pool_create(num_blocks, block_size, _ptr(order, c_i32), ctypes.byref(handle)),
+              "pa_pool_create")
+        self.handle = handle
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self.handle:
+            _lib.pa_pool_destroy(self.handle)
+            self.handle = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, seq, n_tokens):
+        import numpy as np
+        slots = np.empty(max(n_tokens, 0), dtype=np.int64)
+        check(_lib.pa_seq_alloc(self.handle, seq, n_tokens, _ptr(slots, c_i64)), "pa_seq_alloc")
+        return slots
+
+    def append(self, seq):
+        slot, src, dst = c_i64(), c_i32(), c_i32()
+        check(_lib.pa_seq_append(self.handle, seq, ctypes.byref(slot), ctypes.byref(src),
+                                 ctypes.byref(dst)), "pa_seq_append")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def extend(self, seq, n):
+        import numpy as np
+        slots = np.empty(max(n, 0), dtype=np.int64)
+        src, dst = c_i32(), c_i32()
+        check(_lib.pa_seq_extend(self.handle, seq, n, _ptr(slots, c_i64), ctypes.byref(src),
+                                 ctypes.byref(dst)), "pa_seq_extend")
+        return slots, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, parent, child):
+        check(_lib.pa_seq_fork(self.handle, parent, child), "pa_seq_fork")
+
+    def free(self, seq):
+        check(_lib.pa_seq_free(self.handle, seq), "pa_seq_free")
+
+    def seq_len(self, seq):
+        n = c_i32()
+        check(_lib.pa_seq_len(self.handle, seq, ctypes.byref(n)), "pa_seq_len")
+        return n.value
+
+    def block_tables(self, seqs, max_blocks):
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        ctx = np.empty(len(ids), dtype=np.int32)
+        check(_lib.pa_pool_block_tables(self.handle, _ptr(ids, c_i64), len(ids), max_blocks,
+                                        _ptr(tables, c_i32), _ptr(ctx, c_i32)), "pa_pool_block_tables")
+        return tables, ctx
+
+    def stats(self):
+        st = pa_pool_stats_t()
+        check(_lib.pa_pool_stats(self.handle, ctypes.byref(st)), "pa_pool_stats")
+        return {f: getattr(st, f) for f, _ in pa_pool_stats_t._fields_}
+
+    def refcount(self, block):
+        return _lib.pa_pool_refcount(self.handle, block)
+
+    def free_list(self):
+        import numpy as np
+        n = c_i32()
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        check(_lib.pa_pool_free_list(self.handle, _ptr(out, c_i32), self.num_blocks, ctypes.byref(n)),
+              "pa_pool_free_list")
+        return out[:n.value]
+
+
+# ---------------------------------------------------------------------------
+# Device operations on torch tensors
+# ---------------------------------------------------------------------------
+
+def _cache_dims(k_cache):
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be [num_blocks][num_kv_heads][block_size][head_dim]")
+    return k_cache.shape
+
+
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
+    """Scatter [T][Hkv][d] rows into the caches at ``slot_mapping`` (int64)."""
+    nb, hkv, B, d = _cache_dims(k_cache)
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    T = slot_mapping.numel()
+    if k_new.shape != (T, hkv, d) or v_new.shape != (T, hkv, d):
+        raise ValueError("k_new / v_new must be [T][Hkv][d]")
+    for t in (v_cache, k_new, v_new):
+        if t.dtype != k_cache.dtype:
+            raise ValueError("dtype mismatch")
+    check(_lib.pa_write_kv(_dev(k_cache), _dev(v_cache), _dev(k_new), _dev(v_new), _dev(slot_mapping),
+                           T, hkv, d, B, nb, DTYPE_OF[k_cache.dtype],
+                           stream if stream is not None else current_stream()), "pa_write_kv")
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """Copy whole blocks for each (src, dst) row of the int32 ``pairs`` [n][2]."""
+    nb, hkv, B, d = _cache_dims(k_cache)
+    if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise ValueError("pairs must be int32 [n][2]")
+    n = pairs.numel() // 2
+    check(_lib.pa_copy_blocks(_dev(k_cache), _dev(v_cache), _dev(pairs) if n else None, n, hkv, d, B,
+                              nb, DTYPE_OF[k_cache.dtype],
+                              stream if stream is not None else current_stream()), "pa_copy_blocks")
+
+
+def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
+                partition_size=0, workspace=None):
+    nb, hkv, B, d = _cache_dims(k_cache)
+    S, hq, dq = q.shape
+    a = pa_decode_args()
+    a.out = out.data_ptr() if out is not None else None
+    a.out_dtype = DTYPE_OF[out.dtype] if out is not None else PA_F32
+    a.q = q.data_ptr()
+    a.k_cache = k_cache.data_ptr()
+    a.v_cache = v_cache.data_ptr()
+    a.kv_dtype = DTYPE_OF[k_cache.dtype]
+    a.block_tables = block_tables.data_ptr() if block_tables is not None else None
+    a.ctx_lens = ctx_lens.data_ptr() if ctx_lens is not None else None
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = S, hq, hkv, d
+    a.block_size = B
+    a.max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    a.num_blocks = nb
+    a.max_ctx = max_ctx
+    a.scale = scale
+    a.partition_size = partition_size
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def pa_decode_workspace_bytes(args):
+    n = c_sz()
+    check(_lib.pa_decode_workspace_bytes(ctypes.byref(args), ctypes.byref(n)), "pa_decode_workspace_bytes")
+    return n.value
+
+
+def workspace_for(nbytes, device):
+    """A caller-owned device buffer of at least ``nbytes`` (256-byte aligned)."""
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
+              partition_size=0, workspace=None, stream=None):
+    """Paged decode attention into ``out`` ([S][Hq][d], float32 or the cache dtype)."""
+    for t, dt in ((block_tables, torch.int32), (ctx_lens, torch.int32)):
+        if t.dtype != dt:
+            raise ValueError("block_tables and ctx_lens must be int32")
+    for t in (out, q, k_cache, v_cache, block_tables, ctx_lens):
+        _dev(t)
+    a = decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx, partition_size,
+                    workspace)
+    if workspace is None:
+        need = pa_decode_workspace_bytes(a)
+        if need:
+            workspace = workspace_for(need, q.device)
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = workspace.numel()
+    check(_lib.pa_decode(ctypes.byref(a), stream if stream is not None else current_stream()), "pa_decode")
+    return workspace
+
+
+def contig_args(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_size=0, workspace=None):
+    S, hkv, cap, d = k.shape
+    a = pa_contig_args()
+    a.out = out.data_ptr() if out is not None else None
+    a.out_dtype = DTYPE_OF[out.dtype] if out is not None else PA_F32
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.kv_dtype = DTYPE_OF[k.dtype]
+    a.ctx_lens = ctx_lens.data_ptr() if ctx_lens is not None else None
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = q.shape[0], q.shape[1], hkv, d
+    a.capacity, a.max_ctx, a.scale, a.partition_size = cap, max_ctx, scale, partition_size
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def pa_decode_contiguous_workspace_bytes(args):
+    n = c_sz()
+    check(_lib.pa_decode_contiguous_workspace_bytes(ctypes.byref(args), ctypes.byref(n)),
+          "pa_decode_contiguous_workspace_bytes")
+    return n.value
+
+
+def pa_decode_contiguous(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_size=0, workspace=None,
+                         stream=None):
+    """Decode attention on the contiguous layout [S][Hkv][capacity][d]."""
+    for t in (out, q, k, v, ctx_lens):
+        _dev(t)
+    a = contig_args(out, q, k, v, ctx_lens, scale, max_ctx, partition_size, workspace)
+    if workspace is None:
+        need = pa_decode_contiguous_workspace_bytes(a)
+        if need:
+            workspace = workspace_for(need, q.device)
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = workspace.numel()
+    check(_lib.pa_decode_contiguous(ctypes.byref(a), stream if stream is not None else current_stream()),
+          "pa_decode_contiguous")
+    return workspace

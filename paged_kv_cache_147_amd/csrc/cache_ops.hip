@@ -1,0 +1,107 @@
+// KV-cache writes and copy-on-write block copies for gfx950.
+//
+// pa_write_kv puts each new token's K and V rows into the slot the pool gave
+// it: a new token goes into its sequence's last block while that block has
+// room ("vllm-pagedattention" (chenyuan1125.github.io), 页表真正解开的…).
+// pa_copy_blocks duplicates whole blocks before a branch writes into a last
+// block it still shares with others ("vllm-pagedattention", 一块内存，如何安全
+// 地属于多条序列).  Both are pure 16-byte bit moves: one lane per 16 bytes,
+// consecutive lanes on consecutive bytes of a row, so every wave reads and
+// writes whole 128-byte lines.
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One lane per 16-byte chunk of every (token, KV head) row, K and V.
+__global__ __launch_bounds__(kThreads) void write_kv_kernel(
+    char* __restrict__ kc, char* __restrict__ vc, const char* __restrict__ kn,
+    const char* __restrict__ vn, const int64_t* __restrict__ slots, int64_t chunks_per_token,
+    int32_t chunks_per_row, int32_t row_bytes, int32_t block_size, int64_t num_slots,
+    int64_t total_chunks) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= total_chunks) return;
+  const int64_t t = i / chunks_per_token;
+  const int64_t in_tok = i - t * chunks_per_token;  // (kv head, chunk)
+  const int64_t g = in_tok / chunks_per_row;
+  const int64_t ch = in_tok - g * chunks_per_row;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or out of the pool
+  const int64_t blk = slot / block_size;
+  const int64_t row = slot - blk * block_size;
+  const int64_t kv_heads = chunks_per_token / chunks_per_row;
+  const int64_t dst = ((blk * kv_heads + g) * block_size + row) * row_bytes + ch * 16;
+  const int64_t src = i * 16;  // new rows are [T][Hkv][d], densely packed
+  *reinterpret_cast<uint4*>(kc + dst) = *reinterpret_cast<const uint4*>(kn + src);
+  *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(vn + src);
+}
+
+// blockIdx.x: pair, blockIdx.y: 0 = K, 1 = V.  A block of the cache is
+// block_bytes contiguous bytes (all KV heads of one physical block).
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    char* __restrict__ kc, char* __restrict__ vc, const int32_t* __restrict__ pairs,
+    int64_t block_bytes, int32_t num_blocks) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  char* cache = blockIdx.y == 0 ? kc : vc;
+  const uint4* from = reinterpret_cast<const uint4*>(cache + int64_t(src) * block_bytes);
+  uint4* to = reinterpret_cast<uint4*>(cache + int64_t(dst) * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) to[i] = from[i];
+}
+
+pa_status check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, pa_dtype dtype) {
+  if (!valid_dtype(dtype)) return fail(PA_E_UNSUPPORTED, "dtype");
+  if (num_kv_heads <= 0 || num_blocks <= 0) return fail(PA_E_INVAL, "num_kv_heads and num_blocks must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_E_UNSUPPORTED, "block_size must be 8, 16 or 32");
+  return ok();
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pa_dtype dtype, pa_stream stream) {
+  pa_status st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_E_INVAL, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return fail(PA_E_INVAL, "null device pointer");
+  const int32_t row_bytes = head_dim * dtype_bytes(dtype);
+  const int32_t chunks_per_row = row_bytes / 16;
+  const int64_t chunks_per_token = int64_t(num_kv_heads) * chunks_per_row;
+  const int64_t total = chunks_per_token * num_tokens;
+  const int64_t grid = (total + kThreads - 1) / kThreads;
+  if (grid > INT32_MAX) return fail(PA_E_INVAL, "too many tokens for one launch");
+  hipLaunchKernelGGL(write_kv_kernel, dim3(unsigned(grid)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), slot_mapping, chunks_per_token, chunks_per_row,
+                     row_bytes, block_size, int64_t(num_blocks) * block_size, total);
+  return launch_status("write_kv kernel");
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, pa_dtype dtype, pa_stream stream) {
+  pa_status st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (n_pairs < 0) return fail(PA_E_INVAL, "n_pairs must be >= 0");
+  if (n_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !pairs) return fail(PA_E_INVAL, "null device pointer");
+  const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * dtype_bytes(dtype);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(n_pairs), 2), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), pairs, block_bytes, num_blocks);
+  return launch_status("copy_blocks kernel");
+}

@@ -1,0 +1,254 @@
+// Host block pool: free list, per-sequence block tables, reference counts,
+// fork and copy-on-write.
+//
+// The rules follow the pages ("vLLM PagedAttention：大模型推理的显存管理革命"
+// (horeb.top), 分配策略 and 内存共享：写时复制; "vllm-pagedattention"
+// (chenyuan1125.github.io), 页表真正解开的… and 一块内存，如何安全地属于多条序列;
+// "vllm-paged-attention-engine" (aiqz.cc), 分页存储设计 and the allocator of
+// Python 演示):
+//   * n tokens occupy ceil(n / B) blocks;
+//   * blocks leave from the front of the free list and come back at its end;
+//   * a full last block makes growth take one more block;
+//   * fork shares blocks by reference count; a write into a still-shared
+//     last block copies it first; full blocks stay shared;
+//   * refused requests change nothing.
+// The free list is a ring buffer of num_blocks entries: it can never hold more
+// ids than there are blocks, so pushes and pops are O(1) without allocation.
+#include <cstdint>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+#include "status.h"
+
+using pkv::fail;
+using pkv::ok;
+
+namespace {
+
+struct Sequence {
+  std::vector<int32_t> table;  // physical block ids, logical order
+  int64_t len = 0;             // tokens held
+};
+
+}  // namespace
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;     // free list storage
+  int64_t head = 0;              // index of the front entry
+  int64_t count = 0;             // entries on the free list
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Sequence> seqs;
+
+  int32_t pop_front() {
+    int32_t b = ring[head];
+    head = (head + 1) % num_blocks;
+    --count;
+    return b;
+  }
+  void push_back(int32_t b) {
+    ring[(head + count) % num_blocks] = b;
+    ++count;
+  }
+  int64_t slot_of(const Sequence& s, int64_t pos) const {
+    return int64_t(s.table[pos / block_size]) * block_size + pos % block_size;
+  }
+  int64_t blocks_for(int64_t n) const { return (n + block_size - 1) / block_size; }
+};
+
+extern "C" {
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* initial_free_order, pa_pool** out) {
+  if (!out) return fail(PA_E_INVAL, "out is null");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_E_INVAL, "num_blocks and block_size must be positive");
+  if (int64_t(num_blocks) * block_size > INT32_MAX)
+    return fail(PA_E_INVAL, "num_blocks * block_size must stay below 2^31");
+  pa_pool* p = new (std::nothrow) pa_pool;
+  if (!p) return fail(PA_E_INVAL, "out of host memory");
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ring.resize(num_blocks);
+  p->refcount.assign(num_blocks, 0);
+  if (initial_free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return fail(PA_E_INVAL, "initial_free_order is not a permutation of 0..num_blocks-1");
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+  }
+  p->head = 0;
+  p->count = num_blocks;
+  *out = p;
+  return ok();
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+pa_status pa_seq_alloc(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  if (n_tokens < 0) return fail(PA_E_INVAL, "n_tokens must be >= 0");
+  if (pool->seqs.count(seq)) return fail(PA_E_EXISTS, "sequence " + std::to_string(seq));
+  const int64_t want = pool->blocks_for(n_tokens);
+  if (want > pool->count)
+    return fail(PA_E_NOBLOCKS, "need " + std::to_string(want) + " blocks, " +
+                                   std::to_string(pool->count) + " free");
+  Sequence s;
+  s.table.reserve(want);
+  for (int64_t i = 0; i < want; ++i) {
+    int32_t b = pool->pop_front();
+    pool->refcount[b] = 1;
+    s.table.push_back(b);
+  }
+  s.len = n_tokens;
+  if (slots_out)
+    for (int64_t i = 0; i < n_tokens; ++i) slots_out[i] = pool->slot_of(s, i);
+  pool->seqs.emplace(seq, std::move(s));
+  return ok();
+}
+
+pa_status pa_seq_extend(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_out,
+                        int32_t* cow_src, int32_t* cow_dst) {
+  if (cow_src) *cow_src = -1;
+  if (cow_dst) *cow_dst = -1;
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  if (n < 0) return fail(PA_E_INVAL, "n must be >= 0");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  Sequence& s = it->second;
+  if (n == 0) return ok();
+  const int32_t B = pool->block_size;
+  // Blocks this request takes: one copy if the first token lands in a shared,
+  // partly filled last block, plus the new blocks growth needs.
+  const bool copy = (s.len % B != 0) && pool->refcount[s.table.back()] > 1;
+  const int64_t grow = pool->blocks_for(s.len + n) - int64_t(s.table.size());
+  if (grow + (copy ? 1 : 0) > pool->count)
+    return fail(PA_E_NOBLOCKS, "need " + std::to_string(grow + (copy ? 1 : 0)) + " blocks, " +
+                                   std::to_string(pool->count) + " free");
+  if (copy) {
+    int32_t src = s.table.back();
+    int32_t dst = pool->pop_front();
+    pool->refcount[src] -= 1;
+    pool->refcount[dst] = 1;
+    s.table.back() = dst;
+    if (cow_src) *cow_src = src;
+    if (cow_dst) *cow_dst = dst;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t pos = s.len;
+    if (pos % B == 0) {
+      int32_t b = pool->pop_front();
+      pool->refcount[b] = 1;
+      s.table.push_back(b);
+    }
+    if (slots_out) slots_out[i] = pool->slot_of(s, pos);
+    s.len = pos + 1;
+  }
+  return ok();
+}
+
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int64_t* slot_out, int32_t* cow_src,
+                        int32_t* cow_dst) {
+  int64_t slot = -1;
+  pa_status st = pa_seq_extend(pool, seq, 1, &slot, cow_src, cow_dst);
+  if (st == PA_OK && slot_out) *slot_out = slot;
+  return st;
+}
+
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "parent " + std::to_string(parent));
+  if (pool->seqs.count(child)) return fail(PA_E_EXISTS, "child " + std::to_string(child));
+  Sequence c = it->second;  // copy of table and length
+  for (int32_t b : c.table) pool->refcount[b] += 1;
+  pool->seqs.emplace(child, std::move(c));
+  return ok();
+}
+
+pa_status pa_seq_free(pa_pool* pool, int64_t seq) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  for (int32_t b : it->second.table) {
+    if (--pool->refcount[b] == 0) pool->push_back(b);
+  }
+  pool->seqs.erase(it);
+  return ok();
+}
+
+pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len_out) {
+  if (!pool || !len_out) return fail(PA_E_INVAL, "null argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  if (it->second.len > INT32_MAX) return fail(PA_E_INVAL, "length exceeds int32");
+  *len_out = int32_t(it->second.len);
+  return ok();
+}
+
+pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t n,
+                               int32_t max_blocks, int32_t* tables_out, int32_t* ctx_out) {
+  if (!pool || (n > 0 && (!seqs || !tables_out))) return fail(PA_E_INVAL, "null argument");
+  if (n < 0 || max_blocks <= 0) return fail(PA_E_INVAL, "n >= 0 and max_blocks > 0 required");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seqs[i]));
+    const Sequence& s = it->second;
+    if (int64_t(s.table.size()) > max_blocks)
+      return fail(PA_E_INVAL, "sequence " + std::to_string(seqs[i]) + " holds " +
+                                  std::to_string(s.table.size()) + " blocks > max_blocks");
+    if (s.len > INT32_MAX) return fail(PA_E_INVAL, "length exceeds int32");
+    int32_t* row = tables_out + int64_t(i) * max_blocks;
+    for (int32_t j = 0; j < max_blocks; ++j)
+      row[j] = j < int32_t(s.table.size()) ? s.table[j] : -1;
+    if (ctx_out) ctx_out[i] = int32_t(s.len);
+  }
+  return ok();
+}
+
+pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out) {
+  if (!pool || !out) return fail(PA_E_INVAL, "null argument");
+  pa_pool_stats_t st{};
+  st.num_blocks = pool->num_blocks;
+  st.block_size = pool->block_size;
+  st.free_blocks = int32_t(pool->count);
+  for (int32_t c : pool->refcount) {
+    st.used_blocks += c > 0;
+    st.shared_blocks += c > 1;
+  }
+  st.num_seqs = int32_t(pool->seqs.size());
+  for (const auto& kv : pool->seqs) {
+    st.tokens += kv.second.len;
+    st.waste_tokens += int64_t(kv.second.table.size()) * pool->block_size - kv.second.len;
+  }
+  *out = st;
+  return ok();
+}
+
+int32_t pa_pool_refcount(const pa_pool* pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->refcount[block];
+}
+
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out || (cap > 0 && !out) || cap < 0) return fail(PA_E_INVAL, "bad argument");
+  for (int64_t i = 0; i < pool->count && i < cap; ++i)
+    out[i] = pool->ring[(pool->head + i) % pool->num_blocks];
+  *n_out = int32_t(pool->count);
+  return ok();
+}
+
+}  // extern "C"

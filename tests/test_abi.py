@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+arguments on the host before anything reaches the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_147_amd as P
+from paged_kv_cache_147_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared()
+    for must in ("pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_pool_create", "pa_seq_alloc",
+                 "pa_seq_append", "pa_seq_fork", "pa_seq_free", "pa_pool_block_tables",
+                 "pa_decode_contiguous", "pa_pool_stats"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pa_[a-z_]+)$", out, flags=re.M))
+    names = declared()
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(L.EXPORTED) == names
+
+
+def test_library_shares_torchs_hip_runtime():
+    # the binding imports torch first, so libamdhip64.so.7 resolves to torch's copy
+    import torch
+    maps = open("/proc/self/maps").read()
+    hip_libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip_libs) == 1, hip_libs
+    assert os.path.dirname(torch.__file__) in next(iter(hip_libs))
+
+
+def test_status_strings():
+    lib = P.raw()
+    assert lib.pa_version() == 1
+    assert lib.pa_strerror(0) == b"ok"
+    assert lib.pa_strerror(-2) == b"pool exhausted"
+    assert lib.pa_strerror(12345) == b"unknown status"
+
+
+def _args(**kw):
+    a = L.pa_decode_args()
+    base = dict(out=1, out_dtype=L.PA_F32, q=1, k_cache=1, v_cache=1, kv_dtype=L.PA_BF16,
+                block_tables=1, ctx_lens=1, num_seqs=4, num_q_heads=32, num_kv_heads=8,
+                head_dim=128, block_size=16, max_blocks=64, num_blocks=1024, max_ctx=0,
+                scale=0.088, partition_size=0, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), L.PA_E_UNSUPPORTED),
+    (dict(block_size=64), L.PA_E_UNSUPPORTED),
+    (dict(num_q_heads=24), L.PA_E_UNSUPPORTED),      # group of 3
+    (dict(num_q_heads=20), L.PA_E_INVAL),            # not a multiple of 8
+    (dict(kv_dtype=7), L.PA_E_UNSUPPORTED),
+    (dict(out_dtype=L.PA_F16), L.PA_E_UNSUPPORTED),  # f16 out with bf16 cache
+    (dict(partition_size=100), L.PA_E_INVAL),
+    (dict(partition_size=1024), L.PA_E_INVAL),
+    (dict(max_ctx=64 * 16 + 1), L.PA_E_INVAL),
+    (dict(scale=float("inf")), L.PA_E_INVAL),
+    (dict(num_seqs=-1), L.PA_E_INVAL),
+    (dict(max_blocks=0), L.PA_E_INVAL),
+])
+def test_decode_rejects_before_launch(kw, code):
+    lib = P.raw()
+    a = _args(**kw)
+    n = ctypes.c_size_t()
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == code
+    assert lib.pa_decode(ctypes.byref(a), None) == code
+    assert lib.pa_last_error()
+
+
+def test_decode_workspace_sizes():
+    lib = P.raw()
+    n = ctypes.c_size_t()
+    # 64 blocks * 16 = 1024 tokens -> 4 partitions of 256
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args()), ctypes.byref(n)) == 0
+    rows = 4 * 32 * 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
+    # a single partition needs no workspace
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(max_ctx=256)), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # a too-small workspace is refused on the host
+    a = _args(workspace=256, workspace_bytes=16)
+    assert lib.pa_decode(ctypes.byref(a), None) == L.PA_E_INVAL
+
+
+def test_zero_sequences_is_a_no_op():
+    lib = P.raw()
+    assert lib.pa_decode(ctypes.byref(_args(num_seqs=0)), None) == 0
+    assert lib.pa_write_kv(None, None, None, None, None, 0, 8, 128, 16, 64, L.PA_BF16, None) == 0
+    assert lib.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 64, L.PA_BF16, None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 1, 1, 1, 1, 4, 8, 96, 16, 64, L.PA_BF16, None), L.PA_E_UNSUPPORTED),
+    ((1, 1, 1, 1, 1, 4, 8, 128, 12, 64, L.PA_BF16, None), L.PA_E_UNSUPPORTED),
+    ((1, 1, 1, 1, 1, -4, 8, 128, 16, 64, L.PA_BF16, None), L.PA_E_INVAL),
+    ((None, 1, 1, 1, 1, 4, 8, 128, 16, 64, L.PA_BF16, None), L.PA_E_INVAL),
+    ((1, 1, 1, 1, 1, 4, 0, 128, 16, 64, L.PA_BF16, None), L.PA_E_INVAL),
+])
+def test_write_kv_rejects_before_launch(args, code):
+    assert P.raw().pa_write_kv(*args) == code
+
+
+def test_contiguous_rejects_before_launch():
+    lib = P.raw()
+    a = L.pa_contig_args()
+    for k, v in dict(out=1, out_dtype=0, q=1, k=1, v=1, kv_dtype=2, ctx_lens=1, num_seqs=2,
+                     num_q_heads=8, num_kv_heads=8, head_dim=128, capacity=100, max_ctx=0,
+                     scale=0.1, partition_size=0).items():
+        setattr(a, k, v)
+    assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_INVAL   # capacity % 8
+    a.capacity = 1024
+    a.head_dim = 80
+    assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED
