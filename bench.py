@@ -1,0 +1,238 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+One step = the whole decode hot path over one batch: copy-on-write block
+copies (if the step has any), pa_write_kv of every sequence's new token, and
+pa_decode over the batch.  The default workload is the Llama-3.1-8B-like GQA
+layer (32 query / 8 KV heads, head_dim 128, bf16 cache, B = 16, 256
+sequences in groups of 8 sharing a 1008-token prefix, lognormal private
+lengths).  Inputs are resident in HBM before timing starts; steps rotate over
+several copies of the cache so no step finds the previous step's data in the
+caches.
+
+Prints ONE JSON line (rank 0, N = 1): value = logical KV bytes read per step
+/ step time (GB/s).  ``roofline`` is measured live with HIP events around
+every pa_decode launch in the timed region; ``cpu_baseline`` times the float64
+oracle on a bounded sample of the same batch.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak); sequences/sec"
+PEAK_HBM_GBPS = 8000.0
+WORKLOADS = {
+    "llama31_8b_gqa": ("gqa", "Llama-3.1-8B-like GQA decode layer, shared 1008-token prefixes"),
+    "llama31_8b_gqa_noshare": ("gqa_noshare", "same lengths and bytes, every prefix private"),
+    "llama7b_mha": ("llama7b", "Llama-7B-like MHA decode layer"),
+    "sweep_b8": ("sweep8", "ctx 1000 x 128, B=8"),
+    "sweep_b16": ("sweep16", "ctx 1000 x 128, B=16"),
+    "sweep_b32": ("sweep32", "ctx 1000 x 128, B=32"),
+    "llama13b_long": ("long13b", "LLaMA-13B-like MHA layer, ctx 4096 x 32"),
+    "llama13b_beam": ("beam13b", "8 parents x 4 beams at ctx 4096, copy-on-write"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def elem_bytes(dtype):
+    return {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+
+
+def decode_bytes(wl, ctx):
+    """Algorithmic bytes of one pa_decode launch: every KV row of every context
+    once, q, the float32 output, the table entries read and the lengths."""
+    e = elem_bytes(wl.dtype)
+    S, Hq, Hkv, d, B = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    kv = int(sum(ctx)) * 2 * Hkv * d * e
+    other = S * Hq * d * e + S * Hq * d * 4 + sum(4 * ((c + B - 1) // B) for c in ctx) + 4 * S
+    return kv, kv + other
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in ("decode.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_147_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """Per-launch HBM bytes from the committed counter summary, or None when
+    the decode kernel source changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    m = re.search(r"^\|\s*" + re.escape(workload) + r"\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.e+]+)\s*\|",
+                  text, flags=re.M)
+    if not m or m.group(1) != source_digest():
+        return None
+    return float(m.group(2))
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The float64 oracle, as it stands, on the first sequences of the batch
+    until ~budget_s of work; scaled to GB/s of logical KV."""
+    import numpy as np
+
+    from oracle import attention as A
+    from tests._replay import OracleRun
+    run = OracleRun(wl)
+    tables, lens = run.tables(wl)
+    e = elem_bytes(wl.dtype)
+    done, kv, wall, cpu = 0, 0, 0.0, 0.0
+    while done < wl.num_seqs and wall < budget_s:
+        n = min(8, wl.num_seqs - done)
+        sl = slice(done, done + n)
+        t0, c0 = time.perf_counter(), time.process_time()
+        A.paged_decode(wl.q[sl], run.cache.k, run.cache.v, tables[sl], lens[sl], wl.block_size,
+                       wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        kv += int(np.sum(lens[sl])) * 2 * wl.num_kv_heads * wl.head_dim * e
+        done += n
+    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB logical KV), "
+                      f"{wall:.1f} s wall, float64 numpy",
+            "seqs_per_s": round(done / wall, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama31_8b_gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    import workloads as W
+    from tests._native import NativeDeviceRun
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    key, desc = WORKLOADS[args.workload]
+    t0 = time.time()
+    wl = W.CONFIGS[key]()
+    log(f"[bench] workload {wl.name}: generated in {time.time() - t0:.1f}s")
+    run = NativeDeviceRun(wl, device=dev)
+    ctx = run.ctx_host.tolist()
+    kv_bytes, alg_bytes = decode_bytes(wl, ctx)
+    log(f"[bench] cache built; {wl.num_seqs} seqs, KV {kv_bytes / 1e9:.3f} GB logical")
+
+    # The step's own work: copies, then one write of every new token.
+    step_rows = torch.cat([torch.arange(r0, r0 + n) for (_, r0, n) in run.step_writes]).to(dev)
+    step_slots = torch.cat([s for (s, _, _) in run.step_writes])
+    k_new = run.k_rows.index_select(0, step_rows).contiguous()
+    v_new = run.v_rows.index_select(0, step_rows).contiguous()
+    pairs = (torch.tensor(run.step_copies, dtype=torch.int32, device=dev)
+             if run.step_copies else None)
+    replicas = [(run.k_cache, run.v_cache)]
+    for _ in range(args.replicas - 1):
+        replicas.append((run.k_cache.clone(), run.v_cache.clone()))
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    probe = P._lib.decode_args(out, run.q, run.k_cache, run.v_cache, run.tables, run.ctx, wl.scale,
+                               max_ctx=max(ctx), partition_size=args.partition_size)
+    ws = P._lib.workspace_for(P.pa_decode_workspace_bytes(probe), dev)
+    stream = P.current_stream(dev)
+
+    def step(i, ev=None):
+        kc, vc = replicas[i % len(replicas)]
+        if pairs is not None:
+            P.pa_copy_blocks(kc, vc, pairs, stream=stream)
+        P.pa_write_kv(kc, vc, k_new, v_new, step_slots, stream=stream)
+        if ev is not None:
+            ev[0].record()
+        P.pa_decode(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=max(ctx),
+                    partition_size=args.partition_size, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = elapsed * 1e3 / args.steps
+    dec_avg = float(np.mean(dec_ms))
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; pa_decode avg {dec_avg:.4f} ms "
+        f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
+
+    if args.copy_calibration:
+        a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    gbps = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (dec_avg * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": desc, "batch": wl.num_seqs,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.dtype,
+                   "out_dtype": "f32", "ctx_mean": round(float(np.mean(ctx)), 1),
+                   "ctx_max": int(max(ctx)), "kv_bytes_per_step": kv_bytes,
+                   "cache_replicas": len(replicas), "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "seqs_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": "pa_decode (partition + combine launches)",
+                     "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
