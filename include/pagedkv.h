@@ -221,9 +221,12 @@ typedef struct pa_decode_args {
   int32_t max_ctx;             /* 0 or an upper bound on ctx_lens; sizes the grid
                                   (0 means max_blocks * block_size) */
   float scale;                 /* finite, e.g. 1/sqrt(head_dim) */
-  int32_t partition_size;      /* 0 = automatic; else a multiple of 8 and of
+  int32_t partition_size;      /* 0 = automatic (512, 256 or 128 tokens: the
+                                  largest giving >= 2048 sequence x KV head x
+                                  partition units); else a multiple of 8 and of
                                   block_size, at most min(512, 64 * block_size) */
-  void* workspace;             /* device scratch, >= pa_decode_workspace_bytes */
+  void* workspace;             /* device scratch, >= pa_decode_workspace_bytes,
+                                  256-byte aligned */
   size_t workspace_bytes;
 } pa_decode_args;
 /*
@@ -234,7 +237,13 @@ typedef struct pa_decode_args {
  */
 
 /* Workspace bytes pa_decode needs for these arguments (0 when every context
- * fits one partition).  Validates the arguments like pa_decode. */
+ * fits one partition).  Validates the arguments like pa_decode.
+ *
+ * The workspace holds each partition's (max, sum, weighted sum); a second
+ * short launch merges them.  Its contents need no initialisation and are
+ * fully rewritten by each call, so one workspace serves any number of calls
+ * ordered on one stream; two calls running at the same time must not share
+ * one. */
 pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_out);
 pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
 

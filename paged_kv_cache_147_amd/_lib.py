@@ -292,8 +292,10 @@ def pa_decode_workspace_bytes(args):
 
 
 def workspace_for(nbytes, device):
-    """A caller-owned device buffer of at least ``nbytes`` (256-byte aligned)."""
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    """A zero-filled device buffer of at least ``nbytes`` (256-byte aligned, as
+    torch's allocator aligns blocks); reusable across pa_decode calls that are
+    ordered on one stream."""
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,

@@ -25,8 +25,14 @@
 //   * pass 1 streams K and leaves scaled scores in LDS, a softmax step turns
 //     them into weights, pass 2 streams V and accumulates in float32 (the
 //     weights are never rounded to 16 bits);
-//   * partitions of one sequence are merged by decode_combine_kernel with
-//     the log-sum-exp identity.
+//   * when a context spans several partitions, each writes its (max, sum,
+//     weighted sum) to the workspace and decode_combine_kernel merges them
+//     with the log-sum-exp identity, in partition order.  (Merging inside the
+//     same launch would need device-scope release/acquire fences per wave;
+//     on this GPU those write back and invalidate the XCD's L2 and cost far
+//     more than one short extra launch.)
+// Loads are double-buffered: while one buffer of rows is being consumed the
+// next is in flight, and the first V rows are requested before the softmax.
 // Block ids of a partition are fetched once, one per lane, and broadcast
 // with readlane, so each pass's base address is a scalar.
 #include "device_common.h"
@@ -40,9 +46,16 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+// Word 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data
+// format, no swizzle; loads through it are plain byte-addressed loads.
+constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kRowsPerPass = 8;
-constexpr int kAutoPartition = 256;
 constexpr int kMaxPartition = 512;
+// Automatic partition size: the largest of 512 / 256 / 128 tokens that still
+// yields at least this many (sequence, KV head, partition) units, i.e. about
+// eight waves per compute unit of an MI355X (256 CUs).  Longer partitions
+// amortise each wave's fixed costs; enough units keep every CU busy.
+constexpr int64_t kAutoMinUnits = 2048;
 
 // ---- element helpers ------------------------------------------------------
 
@@ -151,6 +164,7 @@ struct DecodeParams {
   float* part_ml;       // [S][Hq][num_parts][2] (max, sum of weights), log2 domain
   int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
   int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
+  int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t block_size;
@@ -164,20 +178,74 @@ struct DecodeParams {
   float scale_log2e;    // scale * log2(e): scores live in the log2 domain
 };
 
-template <class T, int D, int G, bool PAGED>
+// q.K on the matrix cores: for a GQA group (G >= 2) of 16-bit heads, the
+// scores of 16 tokens x G heads are a small dense contraction over head_dim,
+// done as head_dim / 32 v_mfma_f32_16x16x32 steps (A = 16 K rows, B = the
+// group's queries padded to 16 columns).  A 16-token tile must sit inside one
+// block (block_size >= 16, or the contiguous layout).  MHA (G == 1), float32
+// caches and 8-token blocks use packed dot products on the vector ALUs.
+template <class T, int G>
+constexpr bool mfma_capable() { return T::bytes == 2 && G >= 2; }
+
+// Passes (of 8 token rows) held by one V load buffer; two buffers alternate,
+// so up to 2 * passes_per_buffer * 8 rows are in flight per wave.  The
+// vector-ALU score path uses the same buffers for K.
+template <int G>
+constexpr int passes_per_buffer() { return G <= 2 ? 4 : 2; }
+
+// Rows of LDS scores a partition of `part_tokens` tokens needs: both passes
+// run in pairs of buffers (at most 8 passes = 64 rows per pair), so the count
+// is rounded up to 64 rows; 64 more floats serve as a sink for the MFMA
+// lanes that carry padding heads.
+__host__ __device__ constexpr int lds_rows(int part_tokens) { return (part_tokens + 63) / 64 * 64; }
+template <int G>
+__host__ __device__ constexpr int lds_floats(int part_tokens) { return lds_rows(part_tokens) * G + 64; }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_qk(BF16, uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_qk(F16, uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_qk(F32, uint4, uint4, f32x4_t c) { return c; }
+
+// Linear workgroup id -> (KV head, sequence, partition).  KV head varies
+// fastest, partition slowest: every sequence's first partitions are dispatched
+// first, and the workgroups of sequences too short for a high partition index
+// form the tail of the grid, where they exit at once.
+struct Unit { int g, s, part; };
+__device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
+  Unit u;
+  u.g = id % p.num_kv_heads;
+  const int rest = id / p.num_kv_heads;
+  u.s = rest % p.num_seqs;
+  u.part = rest / p.num_seqs;
+  return u;
+}
+
+template <class T, int D, int G, bool PAGED, bool MFMA>
 __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p) {
   constexpr int EPC = 16 / T::bytes;          // elements per 16-byte chunk
   constexpr int ROW_BYTES = D * T::bytes;
   constexpr int NCH = ROW_BYTES / 128;        // chunks per lane per row
   constexpr int NV = NCH * EPC;               // values per lane per row (= D / 8)
-  constexpr int U = (G >= 8) ? 2 : 4;         // passes per load group
+  static_assert(!MFMA || mfma_capable<T, G>(), "MFMA scores need 16-bit data and G >= 2");
+  // V buffers hold 2 passes on the MFMA path, so that both passes cover the
+  // same padded pass count (a multiple of 4).
+  constexpr int U = MFMA ? 2 : passes_per_buffer<G>();
+  constexpr int KK = D / 32;                  // MFMA steps over head_dim
   static_assert(NCH >= 1, "row must span the 8 lanes");
 
-  extern __shared__ float lds[];  // [part_tokens][G]: scores, then weights
+  extern __shared__ float lds[];  // [rows][G] scores, then weights; + 64-float sink
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  const Unit unit = unit_of(blockIdx.x, p);
+  const int g = unit.g, s = unit.s, part = unit.part;
   const int lane = threadIdx.x;
   const int r = lane >> 3;
   const int c = lane & 7;
@@ -212,91 +280,192 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
     }
   }
 
-  // Query chunks matching this lane's K chunks.
-  uint4 qc[G][NCH];
-  {
-    const char* qrow = reinterpret_cast<const char*>(p.q) + head0 * ROW_BYTES + c * 16;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < NCH; ++j)
-        qc[h][j] = *reinterpret_cast<const uint4*>(qrow + h * ROW_BYTES + j * 128);
-  }
-
-  // Byte offset of this lane's row in pass `pass` (pass index is uniform).
-  auto row_offset = [&](int pass) -> int64_t {
-    const int t = tok0 + pass * kRowsPerPass;
+  // First row of pass `pass` (clamped to the last real pass, so padding
+  // passes re-read cached rows) and how many of its 8 rows are in the context.
+  auto pass_rows = [&](const char* base, int pass, int& live_rows) -> const char* {
+    const int t = tok0 + min(pass, npass - 1) * kRowsPerPass;
+    live_rows = min(tok1 - t, kRowsPerPass);
     if constexpr (PAGED) {
       const int lb = (t >> p.log2_block) - (tok0 >> p.log2_block);
       const int phys = __builtin_amdgcn_readlane(lane_block, lb);
-      return (int64_t(phys) * p.num_kv_heads + g) * p.tile_bytes +
-             int64_t((t & (p.block_size - 1)) + r) * ROW_BYTES + c * 16;
+      return base + (int64_t(phys) * p.num_kv_heads + g) * p.tile_bytes +
+             int64_t(t & (p.block_size - 1)) * ROW_BYTES;
     } else {
-      return (int64_t(s) * p.num_kv_heads + g) * p.region_bytes + int64_t(t + r) * ROW_BYTES +
-             c * 16;
+      return base + (int64_t(s) * p.num_kv_heads + g) * p.region_bytes + int64_t(t) * ROW_BYTES;
     }
   };
-  auto load_group = [&](const char* base, uint4 (&buf)[U][NCH], int first_pass) {
+  auto rsrc_of = [](const char* rows, int nrows) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows), 0, nrows * ROW_BYTES, kRawBufferWord3);
+  };
+  auto load16 = [](__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  };
+
+  // Row loads are buffer loads: a scalar resource for a pass's rows plus a
+  // per-lane offset (row r, chunk c) and an immediate per chunk; the hardware
+  // range-checks every load against the resource.  Rows past the context are
+  // never read: their lanes re-read the pass's last real row, and since their
+  // scores are masked to -inf they get weight 0, so the (finite) duplicate
+  // contributes exactly nothing.
+  auto load_buf = [&](const char* base, uint4 (&buf)[U][NCH], int b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pass = min(first_pass + u, npass - 1);  // re-read, never overrun
-      const char* row = base + row_offset(pass);
+      int live;
+      const auto rs = rsrc_of(pass_rows(base, b * U + u, live), kRowsPerPass);
+      const uint32_t off = uint32_t(min(r, live - 1)) * ROW_BYTES + uint32_t(c) * 16;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) buf[u][j] = *reinterpret_cast<const uint4*>(row + j * 128);
+      for (int j = 0; j < NCH; ++j) buf[u][j] = load16(rs, off + j * 128);
     }
   };
 
-  const int ngroups = (npass + U - 1) / U;
-
-  // ---- pass 1: scores ------------------------------------------------------
-  float run_max = -INFINITY;  // over this lane's rows, for head c % G
-  {
-    uint4 cur[U][NCH], nxt[U][NCH];
-    load_group(p.k, cur, 0);
-    for (int gi = 0; gi < ngroups; ++gi) {
-      if (gi + 1 < ngroups) load_group(p.k, nxt, (gi + 1) * U);
+  // ---- pass 1: scores, scaled to the log2 domain, into LDS ----------------
+  float run_max = -INFINITY;
+  uint4 bufA[U][NCH], bufB[U][NCH];
+  if constexpr (MFMA) {
+    // Lane (m = lane % 16, q4 = lane / 16) holds, of token m of a 16-token
+    // tile, elements [32 kk + 8 q4, +8) for step kk -- the A layout of
+    // v_mfma_f32_16x16x32 -- and of query head m the same elements as the B
+    // operand (zero for m >= G).  The result D[4 q4 + i][m] is the score of
+    // token 4 q4 + i for head m.
+    const int m = lane & 15;
+    const int q4 = lane >> 4;
+    uint4 qb[KK];
+    {
+      const char* qrow = reinterpret_cast<const char*>(p.q) + (head0 + min(m, G - 1)) * ROW_BYTES + q4 * 16;
+      const uint32_t keep = m < G ? ~0u : 0u;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrow + kk * 64);
+        qb[kk] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      }
+    }
+    // The two 8-row passes of a tile are consecutive rows of one block (or of
+    // the contiguous region), so one resource spans both.
+    auto load_tile = [&](uint4 (&kt)[KK], int tile) {
+      int live0, live1;
+      const char* rows0 = pass_rows(p.k, 2 * tile, live0);
+      pass_rows(p.k, 2 * tile + 1, live1);
+      const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
+      const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
+      const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
+    };
+    float* sink = lds + lds_rows(p.part_tokens) * G + lane;
+    auto score_tile = [&](const uint4 (&kt)[KK], int tile) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = mfma_qk(T{}, kt[kk], qb[kk], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = tile * 16 + q4 * 4 + i;
+        float sc = acc[i] * p.scale_log2e;
+        if (tok0 + row >= tok1 || m >= G) sc = -INFINITY;  // past the context, or a padding head
+        *(m < G ? lds + row * G + m : sink) = sc;
+        run_max = fmaxf(run_max, sc);
+      }
+    };
+    const int npairs = (npass + 3) / 4;  // pairs of 16-token tiles
+    uint4 ktA[KK], ktB[KK];
+    load_tile(ktA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(ktB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < npairs; ++i) {
+      score_tile(ktA, 2 * i);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(ktA, 2 * i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(ktB, 2 * i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(ktB, 2 * i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // first V rows start streaming while the weights are formed
+    load_buf(p.v, bufA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.v, bufB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // head m's scores sit in lanes m, m+16, m+32, m+48; leave each lane i
+    // with the max of head i % G, as the vector-ALU path does
+    run_max = fmaxf(run_max, __shfl_xor(run_max, 16));
+    run_max = fmaxf(run_max, __shfl_xor(run_max, 32));
+    run_max = __shfl(run_max, lane % G);
+  } else {
+    // Lane (r, c) holds chunks j * 128 + c * 16 of row r of each 8-row pass;
+    // the query chunks matching them stay in registers.
+    uint4 qc[G][NCH];
+    {
+      const char* qrow = reinterpret_cast<const char*>(p.q) + head0 * ROW_BYTES + c * 16;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+          qc[h][j] = *reinterpret_cast<const uint4*>(qrow + h * ROW_BYTES + j * 128);
+    }
+    auto score_buf = [&](const uint4 (&buf)[U][NCH], int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int pass = gi * U + u;
-        if (pass >= npass) break;
+        const int pass = b * U + u;
         float sc[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float a = 0.f;
 #pragma unroll
-          for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, cur[u][j], qc[h][j], a);
+          for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, buf[u][j], qc[h][j], a);
           sc[h] = row8_sum(a);
         }
         float mine = sc[0];
 #pragma unroll
         for (int h = 1; h < G; ++h) mine = (c % G == h) ? sc[h] : mine;
         mine *= p.scale_log2e;
-        const int t = tok0 + pass * kRowsPerPass + r;
-        if (t >= tok1) mine = -INFINITY;
-        if (c < G) lds[(pass * kRowsPerPass + r) * G + c] = mine;
+        if (tok0 + pass * kRowsPerPass + r >= tok1) mine = -INFINITY;  // past the context
+        // lanes c and c + G hold the same head: both store the same value
+        lds[(pass * kRowsPerPass + r) * G + c % G] = mine;
         run_max = fmaxf(run_max, mine);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) cur[u][j] = nxt[u][j];
+    };
+    const int npairs = (npass + 2 * U - 1) / (2 * U);
+    load_buf(p.k, bufA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.k, bufB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // The scheduling barriers keep the order "consume one buffer, refill it,
+    // consume the other, refill it", so one buffer is always in flight.
+    for (int i = 0; i < npairs; ++i) {
+      score_buf(bufA, 2 * i);
+      __builtin_amdgcn_sched_barrier(0);
+      load_buf(p.k, bufA, 2 * i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      score_buf(bufB, 2 * i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_buf(p.k, bufB, 2 * i + 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // first V rows start streaming while the weights are formed
+    load_buf(p.v, bufA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.v, bufB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane i's run_max belongs to head i % G: reduce over that head's lanes
+#pragma unroll
+    for (int mm = G; mm < kWave; mm <<= 1) run_max = fmaxf(run_max, __shfl_xor(run_max, mm));
   }
 
   // ---- softmax weights -----------------------------------------------------
-  // Lane i's run_max belongs to head i % G; reduce over the lanes of that head.
-#pragma unroll
-  for (int m = G; m < kWave; m <<= 1) run_max = fmaxf(run_max, __shfl_xor(run_max, m));
+  // The score pass wrote every row of whole pairs of 2U passes (MFMA: pairs of
+  // 16-token tiles, the same 4 passes); the weights cover exactly those rows.
+  const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
   __syncthreads();
   float wsum = 0.f;
-  const int nent = npass * kRowsPerPass * G;
+  const int nent = npass_v * kRowsPerPass * G;
   for (int e = lane; e < nent; e += kWave) {  // entry e belongs to head e % G = lane % G
     const float w = __builtin_amdgcn_exp2f(lds[e] - run_max);
     lds[e] = w;
     wsum += w;
   }
 #pragma unroll
-  for (int m = G; m < kWave; m <<= 1) wsum += __shfl_xor(wsum, m);
+  for (int mm = G; mm < kWave; mm <<= 1) wsum += __shfl_xor(wsum, mm);
   __syncthreads();
 
   // ---- pass 2: weighted sum of V --------------------------------------------
@@ -305,41 +474,35 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < NV; ++e) acc[h][e] = 0.f;
-  {
-    uint4 cur[U][NCH], nxt[U][NCH];
-    load_group(p.v, cur, 0);
-    for (int gi = 0; gi < ngroups; ++gi) {
-      if (gi + 1 < ngroups) load_group(p.v, nxt, (gi + 1) * U);
+  auto accumulate_buf = [&](const uint4 (&buf)[U][NCH], int b) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int pass = gi * U + u;
-        if (pass >= npass) break;
-        const float* wrow = lds + (pass * kRowsPerPass + r) * G;
-        float w[G];
+    for (int u = 0; u < U; ++u) {
+      const int pass = b * U + u;
+      const float* wrow = lds + (pass * kRowsPerPass + r) * G;
+      float w[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) w[h] = wrow[h];
-        const bool tail = tok0 + (pass + 1) * kRowsPerPass > tok1;
-        const bool live = tok0 + pass * kRowsPerPass + r < tok1;
+      for (int h = 0; h < G; ++h) w[h] = wrow[h];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          float vv[EPC];
-          widen(T{}, cur[u][j], vv);
-          if (tail) {
-            // rows past the context may hold anything (even NaN): select, never multiply
+      for (int j = 0; j < NCH; ++j) {
+        float vv[EPC];
+        widen(T{}, buf[u][j], vv);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) vv[e] = live ? vv[e] : 0.f;
-          }
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[h][j * EPC + e] = fmaf(w[h], vv[e], acc[h][j * EPC + e]);
-        }
+          for (int e = 0; e < EPC; ++e) acc[h][j * EPC + e] = fmaf(w[h], vv[e], acc[h][j * EPC + e]);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) cur[u][j] = nxt[u][j];
     }
+  };
+  const int npairs_v = npass_v / (2 * U);
+  for (int i = 0; i < npairs_v; ++i) {
+    accumulate_buf(bufA, 2 * i);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.v, bufA, 2 * i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate_buf(bufB, 2 * i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.v, bufB, 2 * i + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Sum the 8 row lanes sharing chunk position c (lanes c, c+8, ..., c+56).
@@ -362,8 +525,8 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
     head_m[h] = __shfl(run_max, h);
   }
 
-  // Lane (r, c) writes head r's values at its chunk positions.
   if (nparts_seq == 1) {
+    // Lane (r, c) writes head r's values at its chunk positions.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (r != h) continue;
@@ -384,66 +547,98 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
         }
       }
     }
-  } else {
+    return;
+  }
+
+  // Several partitions: publish this one's (m, l, o) for decode_combine_kernel.
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (r != h) continue;
-      const int64_t prow = (head0 + h) * p.num_parts + part;
-      float* o = p.part_o + prow * D;
+  for (int h = 0; h < G; ++h) {
+    if (r != h) continue;
+    const int64_t prow = (head0 + h) * p.num_parts + part;
+    float* o = p.part_o + prow * D;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int d0 = j * (128 / T::bytes) + c * EPC;
+    for (int j = 0; j < NCH; ++j) {
+      const int d0 = j * (128 / T::bytes) + c * EPC;
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-          *reinterpret_cast<float4*>(o + d0 + e) =
-              make_float4(acc[h][j * EPC + e], acc[h][j * EPC + e + 1], acc[h][j * EPC + e + 2],
-                          acc[h][j * EPC + e + 3]);
-      }
-      if (c == 0) {
-        p.part_ml[prow * 2 + 0] = head_m[h];
-        p.part_ml[prow * 2 + 1] = head_l[h];
-      }
+      for (int e = 0; e < EPC; e += 4)
+        *reinterpret_cast<float4*>(o + d0 + e) =
+            make_float4(acc[h][j * EPC + e], acc[h][j * EPC + e + 1], acc[h][j * EPC + e + 2],
+                        acc[h][j * EPC + e + 3]);
+    }
+    if (c == 0) {
+      p.part_ml[prow * 2 + 0] = head_m[h];
+      p.part_ml[prow * 2 + 1] = head_l[h];
     }
   }
 }
 
-// Merge the partitions of each (sequence, query head):
-//   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p 2^(m_p - M) o_p / L.
-// Partitions are visited in index order, so the result is deterministic.
+// Merges the partitions of each (sequence, query head):
+//   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),  out = sum_i 2^(m_i - M) o_i / L.
+// One wave per (sequence, query head).  Lane i holds partition i's (m, l)
+// (64 partitions per round), so the max and the sum are wave reductions; each
+// lane then owns D / 64 output elements and adds the partitions in index
+// order, so the result never depends on the order in which partitions
+// finished.  Every load address is known up front, so the loads of a round are
+// all in flight together.
 template <class T, int D>
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
-  const int qh = blockIdx.x;
-  const int s = blockIdx.y;
+  const int64_t head = blockIdx.x;  // s * Hq + query head
+  const int s = int(head / p.num_q_heads);
+  const int lane = threadIdx.x;
   const int ctx = min(p.ctx_lens[s], p.max_ctx);
   if (ctx <= 0) return;
   const int np = (ctx + p.part_tokens - 1) / p.part_tokens;
-  if (np <= 1) return;
-  const int64_t head = int64_t(s) * p.num_q_heads + qh;
-  const float* ml = p.part_ml + head * p.num_parts * 2;
-  const float* po = p.part_o + head * p.num_parts * D;
+  if (np <= 1) return;  // the partition kernel wrote this output itself
+  constexpr int PER = D / kWave;  // output values per lane
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + head * p.num_parts;
+  const float* po = p.part_o + head * p.num_parts * D + lane * PER;
+
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[i].x);
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+
   float L = 0.f;
-  for (int i = 0; i < np; ++i) L += ml[2 * i + 1] * __builtin_amdgcn_exp2f(ml[2 * i] - M);
-  const float inv = 1.f / L;
-  constexpr int PER = D / kWave;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * i] - M);
+  for (int base = 0; base < np; base += kWave) {
+    const int n = min(np - base, kWave);
+    const float2 mine = lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.f);
+    const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past n
+    L += mine.y * f;
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+      float x[8][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(f, po[int64_t(i) * D + k * kWave + threadIdx.x], o[k]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) x[u][k] = po[int64_t(base + i + u) * D + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float fu = __shfl(f, i + u);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, x[u][k], o[k]);
+      }
+    }
+    for (; i < n; ++i) {
+      const float fu = __shfl(f, i);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, po[int64_t(base + i) * D + k], o[k]);
+    }
   }
 #pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m);
+  const float inv = 1.f / L;
+  const int64_t obase = head * D + lane * PER;
+#pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int64_t idx = head * D + k * kWave + threadIdx.x;
     const float x = o[k] * inv;
     if constexpr (T::bytes == 4) {
-      reinterpret_cast<float*>(p.out)[idx] = x;
+      reinterpret_cast<float*>(p.out)[obase + k] = x;
     } else {
-      if (p.out_f32) reinterpret_cast<float*>(p.out)[idx] = x;
-      else reinterpret_cast<uint16_t*>(p.out)[idx] = narrow(T{}, x);
+      if (p.out_f32) reinterpret_cast<float*>(p.out)[obase + k] = x;
+      else reinterpret_cast<uint16_t*>(p.out)[obase + k] = narrow(T{}, x);
     }
   }
 }
@@ -462,6 +657,7 @@ struct Plan {
   int max_ctx = 0;
   size_t workspace = 0;
   size_t part_o_bytes = 0;
+  size_t part_ml_bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -470,7 +666,6 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, int block,
                       int ctx_bound, int partition, float scale, Plan* plan) {
   if (S < 0 || Hq <= 0 || Hkv <= 0) return fail(PA_E_INVAL, "num_seqs >= 0, heads > 0 required");
-  if (S > 65535 || Hkv > 65535) return fail(PA_E_UNSUPPORTED, "at most 65535 sequences and KV heads per call");
   if (!valid_dtype(kv)) return fail(PA_E_UNSUPPORTED, "kv dtype");
   if (out != PA_F32 && out != kv) return fail(PA_E_UNSUPPORTED, "out dtype must be f32 or kv dtype");
   if (Hq % Hkv) return fail(PA_E_INVAL, "num_q_heads must be a multiple of num_kv_heads");
@@ -483,39 +678,60 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   const int unit = block > 8 ? block : 8;
   const int cap = block > 0 ? (64 * block < kMaxPartition ? 64 * block : kMaxPartition) : kMaxPartition;
   int pt = partition;
-  if (pt == 0) pt = kAutoPartition;
+  if (pt == 0) {
+    pt = 128;
+    for (int cand : {512, 256}) {
+      if (cand % unit == 0 && cand <= cap &&
+          int64_t(S) * Hkv * ((ctx_bound + cand - 1) / cand) >= kAutoMinUnits) {
+        pt = cand;
+        break;
+      }
+    }
+  }
   if (pt <= 0 || pt % unit || pt > cap)
     return fail(PA_E_INVAL, "partition_size must be a multiple of 8 and of block_size, at most " +
                                 std::to_string(cap));
   plan->part_tokens = pt;
   plan->max_ctx = ctx_bound;
   plan->num_parts = (ctx_bound + pt - 1) / pt;
+  if (int64_t(plan->num_parts) * S * Hkv > INT32_MAX || int64_t(S) * Hq > INT32_MAX)
+    return fail(PA_E_UNSUPPORTED, "too many (partition, sequence, head) units for one launch");
   plan->workspace = 0;
   if (plan->num_parts > 1 && S > 0) {
     const size_t rows = size_t(S) * Hq * plan->num_parts;
     plan->part_o_bytes = align256(rows * D * sizeof(float));
-    plan->workspace = plan->part_o_bytes + align256(rows * 2 * sizeof(float));
+    plan->part_ml_bytes = align256(rows * 2 * sizeof(float));
+    plan->workspace = plan->part_o_bytes + plan->part_ml_bytes;
   }
   return ok();
 }
 
+template <class T, int D, int G, bool PAGED>
+void launch_one(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  const size_t lds = size_t(lds_floats<G>(p.part_tokens)) * sizeof(float);
+  if constexpr (mfma_capable<T, G>()) {
+    if (!PAGED || p.block_size >= 16) {
+      hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PAGED, true>), grid, dim3(kWave), lds, st, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PAGED, false>), grid, dim3(kWave), lds, st, p);
+}
+
 template <class T, int D, bool PAGED>
 pa_status launch_g(const DecodeParams& p, int G, int S, int Hkv, hipStream_t st) {
-  const dim3 grid(p.num_parts, Hkv, S);
-  const size_t lds = size_t(p.part_tokens) * G * sizeof(float);
+  const dim3 grid(unsigned(int64_t(p.num_parts) * S * Hkv));
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_partition_kernel<T, D, 1, PAGED>), grid, dim3(kWave), lds, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_partition_kernel<T, D, 2, PAGED>), grid, dim3(kWave), lds, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_partition_kernel<T, D, 4, PAGED>), grid, dim3(kWave), lds, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_partition_kernel<T, D, 8, PAGED>), grid, dim3(kWave), lds, st, p); break;
+    case 1: launch_one<T, D, 1, PAGED>(p, grid, st); break;
+    case 2: launch_one<T, D, 2, PAGED>(p, grid, st); break;
+    case 4: launch_one<T, D, 4, PAGED>(p, grid, st); break;
+    case 8: launch_one<T, D, 8, PAGED>(p, grid, st); break;
   }
   pa_status ps = launch_status("decode partition kernel");
-  if (ps != PA_OK) return ps;
-  if (p.num_parts > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.num_q_heads, S), dim3(kWave), 0, st, p);
-    return launch_status("decode combine kernel");
-  }
-  return ok();
+  if (ps != PA_OK || p.num_parts <= 1) return ps;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(unsigned(int64_t(S) * p.num_q_heads)), dim3(kWave),
+                     0, st, p);
+  return launch_status("decode combine kernel");
 }
 
 template <bool PAGED>
@@ -592,6 +808,7 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   p.ctx_lens = a->ctx_lens;
   p.part_o = static_cast<float*>(a->workspace);
   p.part_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.part_o_bytes);
+  p.num_seqs = a->num_seqs;
   p.tile_bytes = int64_t(a->block_size) * a->head_dim * eb;
   p.region_bytes = 0;
   p.num_q_heads = a->num_q_heads;
@@ -636,6 +853,7 @@ extern "C" pa_status pa_decode_contiguous(const pa_contig_args* a, pa_stream str
   p.ctx_lens = a->ctx_lens;
   p.part_o = static_cast<float*>(a->workspace);
   p.part_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.part_o_bytes);
+  p.num_seqs = a->num_seqs;
   p.tile_bytes = 0;
   p.region_bytes = int64_t(a->capacity) * a->head_dim * eb;
   p.num_q_heads = a->num_q_heads;

@@ -94,12 +94,14 @@ def test_decode_workspace_sizes():
     lib = P.raw()
     n = ctypes.c_size_t()
     # 64 blocks * 16 = 1024 tokens -> 4 partitions of 256
-    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args()), ctypes.byref(n)) == 0
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(partition_size=256)), ctypes.byref(n)) == 0
     rows = 4 * 32 * 4
     align = lambda x: (x + 255) // 256 * 256
+    # partials: o, then (m, l)
     assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
     # a single partition needs no workspace
-    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(max_ctx=256)), ctypes.byref(n)) == 0
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(max_ctx=256, partition_size=256)),
+                                         ctypes.byref(n)) == 0
     assert n.value == 0
     # a too-small workspace is refused on the host
     a = _args(workspace=256, workspace_bytes=16)
@@ -135,3 +137,20 @@ def test_contiguous_rejects_before_launch():
     a.capacity = 1024
     a.head_dim = 80
     assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("S,hkv,max_ctx,expect_parts", [
+    (256, 8, 4828, 10),     # 256*8*10 units >= 2048 at 512 tokens
+    (128, 8, 1000, 2),      # exactly 2048 units at 512 tokens
+    (64, 8, 1000, 4),       # 1024 units at 512, 2048 at 256
+    (4, 8, 1024, 8),        # small batch: 128-token partitions
+])
+def test_automatic_partition_size(S, hkv, max_ctx, expect_parts):
+    lib = P.raw()
+    n = ctypes.c_size_t()
+    a = _args(num_seqs=S, num_kv_heads=hkv, num_q_heads=4 * hkv, max_blocks=8192 // 16,
+              max_ctx=max_ctx)
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
+    rows = S * 4 * hkv * expect_parts
+    align = lambda x: (x + 255) // 256 * 256
+    assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
