@@ -110,6 +110,73 @@ def cpu_baseline(wl, budget_s=10.0):
             "seqs_per_s": round(done / wall, 2)}
 
 
+def time_calls(fn, n, warm=5):
+    """Average duration (ms) of fn() over n calls, HIP events around each."""
+    import numpy as np
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def compare_contiguous(wl, run, replicas, ws_paged, args, stream):
+    """Paged decode vs the same attention on the contiguous layout (identical
+    logical K/V), and vs the paged kernel with blocks placed in order; all
+    three timed the same way (pa_decode* alone, rotating cache copies)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    from tests._native import NativeDeviceRun, device_tensor
+    from tests._replay import contiguous_layout
+    dev = run.q.device
+    ctx = run.ctx_host
+    cap = int((ctx.max() + 7) // 8 * 8)
+    k, v, _ = contiguous_layout(wl, capacity=cap)
+    reps = [(device_tensor(k, wl.dtype, dev), device_tensor(v, wl.dtype, dev))]
+    for _ in range(args.replicas - 1):
+        reps.append((reps[0][0].clone(), reps[0][1].clone()))
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    ws = [None]
+
+    def paged(i):
+        kc, vc = replicas[i % len(replicas)]
+        P.pa_decode(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=int(ctx.max()),
+                    partition_size=args.partition_size, workspace=ws_paged, stream=stream)
+    paged_ms = time_calls(paged, args.steps)
+
+    def contig(i):
+        kc, vc = reps[i % len(reps)]
+        ws[0] = P.pa_decode_contiguous(out, run.q, kc, vc, run.ctx, wl.scale, max_ctx=int(ctx.max()),
+                                       partition_size=args.partition_size, workspace=ws[0], stream=stream)
+    contig_ms = time_calls(contig, args.steps)
+    del reps
+    # paged kernel, blocks in table order (free list 0..n-1): same lookups, contiguous placement
+    wl_id = type(wl)(**{**wl.__dict__, "free_order": np.arange(wl.num_blocks, dtype=np.int32)})
+    run_id = NativeDeviceRun(wl_id, device=dev)
+    reps_id = [(run_id.k_cache, run_id.v_cache)] + [(run_id.k_cache.clone(), run_id.v_cache.clone())
+                                                   for _ in range(args.replicas - 1)]
+    ws_id = [None]
+
+    def paged_identity(i):
+        kc, vc = reps_id[i % len(reps_id)]
+        ws_id[0] = P.pa_decode(out, run_id.q, kc, vc, run_id.tables, run_id.ctx, wl.scale,
+                               max_ctx=int(ctx.max()), partition_size=args.partition_size,
+                               workspace=ws_id[0], stream=stream)
+    ident_ms = time_calls(paged_identity, args.steps)
+    return {"paged_ms": round(paged_ms, 5), "contiguous_ms": round(contig_ms, 5),
+            "paged_identity_placement_ms": round(ident_ms, 5),
+            "overhead_vs_contiguous": round(paged_ms / contig_ms - 1, 4),
+            "overhead_identity_vs_contiguous": round(ident_ms / contig_ms - 1, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +188,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--compare-contiguous", action="store_true",
+                    help="also time pa_decode_contiguous on the same logical K/V and the paged "
+                         "kernel with blocks placed in order (identity free list); adds a "
+                         "'paged_vs_contiguous' object to the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
@@ -198,6 +269,10 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
+    comparison = None
+    if args.compare_contiguous:
+        comparison = compare_contiguous(wl, run, replicas, ws, args, stream)
+
     gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
@@ -228,6 +303,8 @@ def main():
                      "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg_bytes},
         "cpu_baseline": None,
     }
+    if comparison is not None:
+        result["paged_vs_contiguous"] = comparison
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -30,7 +30,7 @@ Rules, each with the passage it comes from:
   shared ("vllm-pagedattention", 一块内存，如何安全地属于多条序列;
   "vLLM PagedAttention：大模型推理的显存管理革命", 内存共享：写时复制).
 
-Readings where the pages are silent (listed in the design doc as well):
+Readings taken where the pages are silent:
 * slot of token i = block_table[i // B] * B + i % B (flat slot index);
 * a fork copies the parent's table and length and bumps every refcount;
 * freeing walks the table in order, so released blocks reach the free list

@@ -215,17 +215,31 @@ __device__ __forceinline__ f32x4_t mfma_qk(F16, uint4 a, uint4 b, f32x4_t c) {
 }
 __device__ __forceinline__ f32x4_t mfma_qk(F32, uint4, uint4, f32x4_t c) { return c; }
 
-// Linear workgroup id -> (KV head, sequence, partition).  KV head varies
-// fastest, partition slowest: every sequence's first partitions are dispatched
-// first, and the workgroups of sequences too short for a high partition index
-// form the tail of the grid, where they exit at once.
+// Linear workgroup id -> (KV head, sequence, partition).
+// * KV head varies fastest: consecutive workgroups go to the 8 XCDs in turn,
+//   so with Hkv a multiple of 8 each XCD serves a fixed set of KV heads for
+//   every sequence and all XCDs get the same work.
+// * Sequences are taken in chunks of kSeqChunk; inside a chunk, partition
+//   varies slowest.  Sequences that share prefix blocks (forks, beams) sit
+//   next to each other, so their reads of the same (block, head) tile happen
+//   at about the same time on the same XCD and hit its L2, while the working
+//   set of a chunk stays within that L2.
+// * Partitions past a sequence's end exit at once; they fall at the end of
+//   each chunk rather than on particular XCDs.
+constexpr int kSeqChunk = 32;
 struct Unit { int g, s, part; };
 __device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
   Unit u;
   u.g = id % p.num_kv_heads;
   const int rest = id / p.num_kv_heads;
-  u.s = rest % p.num_seqs;
-  u.part = rest / p.num_seqs;
+  const int chunk = rest / (kSeqChunk * p.num_parts);
+  const int within = rest % (kSeqChunk * p.num_parts);
+  u.part = within / kSeqChunk;
+  u.s = chunk * kSeqChunk + within % kSeqChunk;
+  if (u.s >= p.num_seqs) {  // padding of the last chunk: an empty unit
+    u.s = 0;
+    u.part = p.num_parts;
+  }
   return u;
 }
 
@@ -236,9 +250,8 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
   constexpr int NCH = ROW_BYTES / 128;        // chunks per lane per row
   constexpr int NV = NCH * EPC;               // values per lane per row (= D / 8)
   static_assert(!MFMA || mfma_capable<T, G>(), "MFMA scores need 16-bit data and G >= 2");
-  // V buffers hold 2 passes on the MFMA path, so that both passes cover the
-  // same padded pass count (a multiple of 4).
   constexpr int U = MFMA ? 2 : passes_per_buffer<G>();
+  constexpr int KT = 1;  // 16-token score tiles per K buffer (MFMA path)
   constexpr int KK = D / 32;                  // MFMA steps over head_dim
   static_assert(NCH >= 1, "row must span the 8 lanes");
 
@@ -365,20 +378,28 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
         run_max = fmaxf(run_max, sc);
       }
     };
-    const int npairs = (npass + 3) / 4;  // pairs of 16-token tiles
-    uint4 ktA[KK], ktB[KK];
-    load_tile(ktA, 0);
+    auto load_tiles = [&](uint4 (&kt)[KT][KK], int b) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) load_tile(kt[t], b * KT + t);
+    };
+    auto score_tiles = [&](const uint4 (&kt)[KT][KK], int b) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) score_tile(kt[t], b * KT + t);
+    };
+    const int npairs = (npass + 4 * KT - 1) / (4 * KT);  // pairs of K buffers
+    uint4 ktA[KT][KK], ktB[KT][KK];
+    load_tiles(ktA, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(ktB, 1);
+    load_tiles(ktB, 1);
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 0; i < npairs; ++i) {
-      score_tile(ktA, 2 * i);
+      score_tiles(ktA, 2 * i);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(ktA, 2 * i + 2);
+      load_tiles(ktA, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      score_tile(ktB, 2 * i + 1);
+      score_tiles(ktB, 2 * i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(ktB, 2 * i + 3);
+      load_tiles(ktB, 2 * i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // first V rows start streaming while the weights are formed
@@ -453,14 +474,17 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
   }
 
   // ---- softmax weights -----------------------------------------------------
-  // The score pass wrote every row of whole pairs of 2U passes (MFMA: pairs of
-  // 16-token tiles, the same 4 passes); the weights cover exactly those rows.
+  // The V pass runs whole pairs of 2U passes; the score pass wrote whole
+  // pairs of 16-token tiles (MFMA) or the same 2U-pass pairs.  Rows the V pass
+  // reaches beyond the written scores are padding and get weight 0.
   const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
+  const int rows_k = MFMA ? (npass + 4 * KT - 1) / (4 * KT) * (32 * KT) : npass_v * kRowsPerPass;
   __syncthreads();
   float wsum = 0.f;
   const int nent = npass_v * kRowsPerPass * G;
+  const int nent_k = rows_k * G;
   for (int e = lane; e < nent; e += kWave) {  // entry e belongs to head e % G = lane % G
-    const float w = __builtin_amdgcn_exp2f(lds[e] - run_max);
+    const float w = e < nent_k ? __builtin_amdgcn_exp2f(lds[e] - run_max) : 0.f;
     lds[e] = w;
     wsum += w;
   }
@@ -694,7 +718,7 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   plan->part_tokens = pt;
   plan->max_ctx = ctx_bound;
   plan->num_parts = (ctx_bound + pt - 1) / pt;
-  if (int64_t(plan->num_parts) * S * Hkv > INT32_MAX || int64_t(S) * Hq > INT32_MAX)
+  if (int64_t(plan->num_parts) * (int64_t(S) + kSeqChunk) * Hkv > INT32_MAX || int64_t(S) * Hq > INT32_MAX)
     return fail(PA_E_UNSUPPORTED, "too many (partition, sequence, head) units for one launch");
   plan->workspace = 0;
   if (plan->num_parts > 1 && S > 0) {
@@ -720,7 +744,8 @@ void launch_one(const DecodeParams& p, dim3 grid, hipStream_t st) {
 
 template <class T, int D, bool PAGED>
 pa_status launch_g(const DecodeParams& p, int G, int S, int Hkv, hipStream_t st) {
-  const dim3 grid(unsigned(int64_t(p.num_parts) * S * Hkv));
+  const int64_t seqs_padded = (int64_t(S) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
+  const dim3 grid(unsigned(int64_t(p.num_parts) * seqs_padded * Hkv));
   switch (G) {
     case 1: launch_one<T, D, 1, PAGED>(p, grid, st); break;
     case 2: launch_one<T, D, 2, PAGED>(p, grid, st); break;
