@@ -196,11 +196,26 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
  * weighted sum of V; the attention itself is unchanged).  The new token must
  * have been written already (it attends to itself).
  *
- * Contexts longer than partition_size are cut into partitions that are
- * reduced independently and merged with the log-sum-exp identity (needs the
- * workspace).  Arithmetic is float32 (16-bit inputs are widened exactly);
- * results do not depend on which physical blocks hold the tokens, and are
- * bitwise reproducible for a given (shape, partition_size).
+ * Contexts are cut into pieces that are reduced independently and merged
+ * with the log-sum-exp identity (which needs the workspace).  Two ways of
+ * cutting them (partition_size):
+ *   >= 0 fixed partitions, one wave each, as on the pages (vLLM's
+ *        partitioned kernel): a sequence's result depends only on its own
+ *        inputs.  0 picks the length automatically (512, 256 or 128 tokens:
+ *        the largest giving >= 2048 sequence x KV head x partition units).
+ *   -1   balanced: the (KV head, sequence) token ranges of the whole batch,
+ *        laid end to end in 16-token tiles, are cut into equal pieces, one
+ *        per wave the GPU holds at once, so every compute unit streams the
+ *        same number of bytes.  The cut depends on all context lengths of
+ *        the batch and on the GPU's wave count (see pa_decode_set_waves).
+ *        A few per cent faster on batches of private contexts; much slower
+ *        when sequences share blocks (forks, beams), which the fixed grid
+ *        reads for all sharers at once.
+ * Arithmetic is float32 (16-bit inputs are widened exactly); results do not
+ * depend on which physical blocks hold the tokens, and are bitwise
+ * reproducible for the same inputs on the same GPU with the same
+ * partition_size (the contiguous entry point cuts identically, so it agrees
+ * bit for bit when both use the same score path).
  */
 typedef struct pa_decode_args {
   void* out;                   /* [S][Hq][head_dim], out_dtype */
@@ -221,10 +236,10 @@ typedef struct pa_decode_args {
   int32_t max_ctx;             /* 0 or an upper bound on ctx_lens; sizes the grid
                                   (0 means max_blocks * block_size) */
   float scale;                 /* finite, e.g. 1/sqrt(head_dim) */
-  int32_t partition_size;      /* 0 = automatic (512, 256 or 128 tokens: the
-                                  largest giving >= 2048 sequence x KV head x
-                                  partition units); else a multiple of 8 and of
-                                  block_size, at most min(512, 64 * block_size) */
+  int32_t partition_size;      /* 0 = automatic fixed partitions, -1 = balanced
+                                  schedule, else fixed partitions of that many
+                                  tokens: a multiple of 8 and of block_size, at
+                                  most min(512, 64 * block_size) */
   void* workspace;             /* device scratch, >= pa_decode_workspace_bytes,
                                   256-byte aligned */
   size_t workspace_bytes;
@@ -236,14 +251,18 @@ typedef struct pa_decode_args {
  * never read outside the caches (its sequence's output is then meaningless).
  */
 
-/* Workspace bytes pa_decode needs for these arguments (0 when every context
- * fits one partition).  Validates the arguments like pa_decode.
+/* Workspace bytes pa_decode needs for these arguments.  Validates the
+ * arguments like pa_decode; needs no GPU.
  *
- * The workspace holds each partition's (max, sum, weighted sum); a second
- * short launch merges them.  Its contents need no initialisation and are
- * fully rewritten by each call, so one workspace serves any number of calls
- * ordered on one stream; two calls running at the same time must not share
- * one. */
+ * Fixed partitions: each partition's (max, sum, weighted sum), or 0 bytes
+ * when every context fits one partition.  Balanced (-1): the schedule (per
+ * sequence tile offsets, each piece's first sequence) and two (max, sum,
+ * weighted sum) records per piece, sized for at most
+ * min(8192, num_seqs * num_kv_heads * ceil(max_ctx / 16) / 8) pieces.  A
+ * short launch after the decode kernel merges the records.  The contents need
+ * no initialisation and are rewritten by each call, so one workspace serves
+ * any number of calls ordered on one stream; two calls running at the same
+ * time must not share one. */
 pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_out);
 pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
 
@@ -268,13 +287,24 @@ typedef struct pa_contig_args {
   int32_t capacity;            /* token rows reserved per (sequence, KV head) */
   int32_t max_ctx;             /* 0 or an upper bound on ctx_lens (0 = capacity) */
   float scale;
-  int32_t partition_size;      /* 0 = automatic; multiple of 8, at most 512 */
+  int32_t partition_size;      /* as in pa_decode_args; fixed partitions a
+                                  multiple of 8, at most 512 */
   void* workspace;
   size_t workspace_bytes;
 } pa_contig_args;
 
 pa_status pa_decode_contiguous_workspace_bytes(const pa_contig_args* args, size_t* bytes_out);
 pa_status pa_decode_contiguous(const pa_contig_args* args, pa_stream stream);
+
+/*
+ * Waves the balanced schedule cuts the work into, for this process: 0 =
+ * automatic (compute units x waves of the decode kernel one compute unit
+ * holds, which keeps every CU streaming to the end), else rounded down to a
+ * multiple of 8 in [8, 8192].  Fewer waves leave room for other kernels
+ * running at the same time.  Takes effect for calls made after it; returns
+ * the previous setting.
+ */
+int pa_decode_set_waves(int32_t waves);
 
 #ifdef __cplusplus
 }

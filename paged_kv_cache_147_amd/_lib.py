@@ -34,7 +34,7 @@ class PagedKVError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_147_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python paged_kv_cache_147_amd/build.py` "
             "(the decode path has no fallback)")
     return ctypes.CDLL(LIB_PATH)
 
@@ -91,6 +91,7 @@ _SIGS = {
     "pa_decode": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
     "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
     "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
+    "pa_decode_set_waves": (c_i32, [c_i32]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -356,3 +357,9 @@ def pa_decode_contiguous(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_siz
     check(_lib.pa_decode_contiguous(ctypes.byref(a), stream if stream is not None else current_stream()),
           "pa_decode_contiguous")
     return workspace
+
+
+def pa_decode_set_waves(waves):
+    """Waves the balanced schedule cuts the work into (0 = automatic); returns
+    the previous setting."""
+    return int(_lib.pa_decode_set_waves(int(waves)))

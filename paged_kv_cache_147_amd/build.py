@@ -1,6 +1,7 @@
 """Build libpagedkv.so (host pool + gfx950 kernels) in-tree with hipcc.
 
-Run as ``python -m paged_kv_cache_147_amd.build`` or through
+Run as ``python paged_kv_cache_147_amd/build.py`` (no package import, so a stale
+library is never loaded first) or through
 ``__graft_entry__.build()``.  Objects go to ``_build/`` at the repository
 root; the shared library lands next to this file, where the binding loads it.
 """

@@ -37,7 +37,11 @@
 // with readlane, so each pass's base address is a scalar.
 #include "device_common.h"
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <map>
+#include <mutex>
 
 namespace pkv {
 namespace {
@@ -51,11 +55,13 @@ constexpr int kWave = 64;
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kRowsPerPass = 8;
 constexpr int kMaxPartition = 512;
-// Automatic partition size: the largest of 512 / 256 / 128 tokens that still
-// yields at least this many (sequence, KV head, partition) units, i.e. about
-// eight waves per compute unit of an MI355X (256 CUs).  Longer partitions
-// amortise each wave's fixed costs; enough units keep every CU busy.
+// partition_size 0: fixed partitions of the largest of 512 / 256 / 128 tokens
+// that still yields at least this many (sequence, KV head, partition) units,
+// about eight waves per compute unit of an MI355X (256 CUs).  Longer
+// partitions amortise each wave's fixed costs; enough units keep every CU
+// busy.
 constexpr int64_t kAutoMinUnits = 2048;
+constexpr int kBalanced = -1;  // partition_size value selecting the balanced schedule
 
 // ---- element helpers ------------------------------------------------------
 
@@ -121,18 +127,6 @@ __device__ __forceinline__ uint16_t narrow(BF16, float x) {
   return uint16_t(u >> 16);
 }
 
-// Eight float32 values -> eight 16-bit outputs in one 16-byte store.
-template <class T>
-__device__ __forceinline__ void store_narrow(T, uint16_t* o, const float* a, float inv) {
-  if constexpr (T::bytes == 2) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = uint32_t(narrow(T{}, a[2 * i] * inv)) | (uint32_t(narrow(T{}, a[2 * i + 1] * inv)) << 16);
-    *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Lane-exchange steps within the 8 lanes of a row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -151,7 +145,88 @@ __device__ __forceinline__ float row8_sum(float x) {
   return x;
 }
 
+// Sum over the 8 lanes of each position c (lanes c, c + 8, ..., c + 56) of
+// V values per lane, scattered: afterwards lane (r = lane / 8, c) holds in
+// x[0, V / 8) the sums of values [r V / 8, (r + 1) V / 8).  Three halving
+// steps across lane distance 32, 16 and 8; a step pairs value i with value
+// i + n / 2 and keeps the first sum in the lanes with that lane bit clear,
+// the second in the others.  The distance-32 and -16 steps use the gfx950
+// permlane swaps (after swap(a, b) the two results add to a + a' in the low
+// lanes and b' + b in the high ones), the distance-8 step a DPP rotation
+// within 16-lane rows; all stay on the vector ALU.
+template <int V>
+__device__ __forceinline__ void reduce_scatter8(float (&x)[V], int lane) {
+  static_assert(V % 8 == 0, "8 lanes share each position");
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + V / 2]), false, false);
+    x[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + V / 4]), false, false);
+    x[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  }
+  const bool hi = lane & 8;
+#pragma unroll
+  for (int i = 0; i < V / 8; ++i) {
+    const float a = x[i], b = x[i + V / 8];
+    x[i] = (hi ? b : a) + dpp<kRowRor8>(hi ? a : b);
+  }
+}
+
+// x, hidden from the optimiser: values computed from it are recomputed where
+// they are used instead of being hoisted out of loops and kept in registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// N consecutive float32 values a[i] * s to o (N a power of 2).
+template <int N>
+__device__ __forceinline__ void store_run(float* o, const float* a, float s) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<float4*>(o + i) = make_float4(a[i] * s, a[i + 1] * s, a[i + 2] * s, a[i + 3] * s);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(o) = make_float2(a[0] * s, a[1] * s);
+  } else {
+    *o = a[0] * s;
+  }
+}
+// The same, rounded to 16 bits.
+template <class T, int N>
+__device__ __forceinline__ void store_run(T, uint16_t* o, const float* a, float s) {
+  if constexpr (N == 1) {
+    *o = narrow(T{}, a[0] * s);
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i)
+      w[i] = uint32_t(narrow(T{}, a[2 * i] * s)) | (uint32_t(narrow(T{}, a[2 * i + 1] * s)) << 16);
+    if constexpr (N == 2) {
+      *reinterpret_cast<uint32_t*>(o) = w[0];
+    } else if constexpr (N == 4) {
+      *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N / 2; i += 4) *reinterpret_cast<uint4*>(o + 2 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+    }
+  }
+}
+
 // ---- kernels ----------------------------------------------------------------
+
+// Header of the balanced schedule, written by decode_plan_kernel.
+struct Sched {
+  int64_t total;           // tiles over all (KV head, sequence) ranges
+  int32_t tiles_per_head;  // tiles over all sequences of one KV head
+  int32_t pieces;          // pieces (= waves with work); 0 when there is no context
+};
+constexpr int kTile = 16;             // tokens per schedule tile
+constexpr int kMinTilesPerPiece = 8;  // fewer pieces than waves when the batch is small
+constexpr int kMaxWaves = 8192;       // pieces the workspace is sized for, at most
 
 struct DecodeParams {
   void* out;
@@ -160,8 +235,11 @@ struct DecodeParams {
   const char* v;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* part_o;        // [S][Hq][num_parts][D] unnormalised partition sums
-  float* part_ml;       // [S][Hq][num_parts][2] (max, sum of weights), log2 domain
+  float* part_o;        // fixed: [S][Hq][num_parts][D]; balanced: [2 pieces][G][D] unnormalised sums
+  float* part_ml;       // same rows, (max, sum of weights) in the log2 domain
+  Sched* sched;         // balanced: schedule header
+  int32_t* cum;         // balanced: [S + 1] tiles of the sequences before s (per KV head)
+  int32_t* start_seq;   // balanced: [pieces] sequence holding each piece's first tile
   int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
   int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
   int32_t num_seqs;
@@ -172,8 +250,9 @@ struct DecodeParams {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t max_ctx;
-  int32_t part_tokens;
+  int32_t part_tokens;  // fixed: partition length; balanced: chunk length
   int32_t num_parts;
+  int32_t num_waves;    // balanced: upper bound on pieces (waves launched, rounded up to 8)
   int32_t out_f32;
   float scale_log2e;    // scale * log2(e): scores live in the log2 domain
 };
@@ -200,6 +279,12 @@ constexpr int passes_per_buffer() { return G <= 2 ? 4 : 2; }
 __host__ __device__ constexpr int lds_rows(int part_tokens) { return (part_tokens + 63) / 64 * 64; }
 template <int G>
 __host__ __device__ constexpr int lds_floats(int part_tokens) { return lds_rows(part_tokens) * G + 64; }
+// Balanced schedule: chunks of kBalancedChunk tokens, plus G * D floats of
+// running sums.  448 keeps a GQA group of 4 at d = 128 under 10 KB of LDS,
+// so 16 waves fit a CU's 160 KB.
+constexpr int kBalancedChunk = 448;
+template <int G, int D>
+__host__ __device__ constexpr int lds_floats_balanced() { return lds_floats<G>(kBalancedChunk) + G * D; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -213,9 +298,29 @@ __device__ __forceinline__ f32x4_t mfma_qk(F16, uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma_qk(F32, uint4, uint4, f32x4_t c) { return c; }
 
-// Linear workgroup id -> (KV head, sequence, partition).
+// ---- schedules ---------------------------------------------------------------
+//
+// Fixed partitions (partition_size >= 0, the default): one wave per
+// (partition, KV head, sequence), partition = a fixed number of tokens, as on
+// the pages; the hardware dispatcher hands units to CUs as slots free up.
+//
+// Balanced (partition_size == -1): the (KV head, sequence) token ranges are
+// laid end to end in 16-token tiles, KV head major, and cut into as many equal
+// contiguous pieces as the GPU holds waves at once; each wave streams one
+// piece, so every CU is handed the same bytes.  A wave's piece covers whole
+// sequences (finished and written directly) and at most two cut ones (its
+// first and its last); a cut sequence leaves one (max, sum, weighted sum)
+// record per piece, merged by the combine kernel in token order.
+// Measured on MI355X it gains a few per cent on batches with private
+// contexts and loses heavily when sequences share blocks: equal pieces start
+// at unrelated token offsets, so sequences that share a prefix read it at
+// different times and miss in L2, where the fixed grid reads it for all of
+// them at once.  It is also limited by the order in which a SIMD serves its
+// waves: the oldest wave issues first, so of four equal pieces on one SIMD
+// the first finishes in about half the time of the last.
+
+// Linear workgroup id -> (KV head, sequence, partition), fixed partitions.
 // * KV head varies fastest: consecutive workgroups go to the 8 XCDs in turn,
 //   so with Hkv a multiple of 8 each XCD serves a fixed set of KV heads for
 //   every sequence and all XCDs get the same work.
@@ -243,8 +348,32 @@ __device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
   return u;
 }
 
-template <class T, int D, int G, bool PAGED, bool MFMA>
-__global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p) {
+// Piece k of the balanced schedule covers flattened tiles
+// [piece_start(k), piece_start(k + 1)); piece_of(pos) is the piece holding
+// tile pos.  Both are exact integer formulas, so every kernel agrees on them.
+__device__ __forceinline__ int64_t piece_start(int64_t k, const Sched& sc) {
+  return k * sc.total / sc.pieces;
+}
+__device__ __forceinline__ int64_t piece_of(int64_t pos, const Sched& sc) {
+  return ((pos + 1) * sc.pieces - 1) / sc.total;
+}
+
+// Workgroup id -> piece.  Workgroups are dealt to the 8 XCDs in turn, so XCD x
+// runs ids x, x + 8, ...; giving it pieces [x * per, (x + 1) * per) keeps one
+// contiguous eighth of the tile order -- the same KV heads, neighbouring
+// sequences -- on one XCD's L2.  Returns -1 for an idle workgroup.
+__device__ __forceinline__ int piece_of_workgroup(int id, const Sched& sc) {
+  const int per = (sc.pieces + 7) / 8;
+  const int j = id / 8;
+  const int k = (id % 8) * per + j;
+  return (j < per && k < sc.pieces) ? k : -1;
+}
+
+// 16-bit caches with G <= 4 fit 128 registers, i.e. 4 waves per SIMD (the
+// balanced schedule's loops need the hint to get there without spilling).
+template <class T, int D, int G, bool PAGED, bool MFMA, bool BAL>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(T::bytes == 2 && G <= 4 ? 4 : 1)))
+void decode_kernel(DecodeParams p) {
   constexpr int EPC = 16 / T::bytes;          // elements per 16-byte chunk
   constexpr int ROW_BYTES = D * T::bytes;
   constexpr int NCH = ROW_BYTES / 128;        // chunks per lane per row
@@ -257,41 +386,49 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
 
   extern __shared__ float lds[];  // [rows][G] scores, then weights; + 64-float sink
 
-  const Unit unit = unit_of(blockIdx.x, p);
-  const int g = unit.g, s = unit.s, part = unit.part;
-  const int lane = threadIdx.x;
-  const int r = lane >> 3;
-  const int c = lane & 7;
+  const int lane_id = threadIdx.x;
+  // Lane coordinates: (r, c) = (lane / 8, lane % 8) for row work, (m, q4) =
+  // (lane % 16, lane / 16) for matrix-core tiles.  They are re-derived at the
+  // start of every chunk and finish (refresh_lane) from an opaque copy of the
+  // lane id, so addresses built from them are not hoisted out of the range
+  // and chunk loops, where they would hold registers across every pass.
+  int lane = lane_id, r = lane >> 3, c = lane & 7, m = lane & 15, q4 = lane >> 4;
 
-  const int ctx = min(p.ctx_lens[s], p.max_ctx);
-  const int64_t head0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;  // first query row
-  if (ctx <= 0) {
-    // no context: defined as a zero output row
-    if (part == 0) {
-      for (int i = lane; i < G * D; i += kWave) {
-        if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[head0 * D + i] = 0.f;
-        else reinterpret_cast<uint16_t*>(p.out)[head0 * D + i] = 0;
-      }
-    }
-    return;
-  }
-  const int tok0 = part * p.part_tokens;
-  if (tok0 >= ctx) return;
-  const int tok1 = min(tok0 + p.part_tokens, ctx);
-  const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
-  const int npass = (tok1 - tok0 + kRowsPerPass - 1) / kRowsPerPass;
-
-  // Physical ids of this partition's blocks, one per lane (clamped into the
-  // pool so a corrupt table cannot read outside the caches).
+  // The range being reduced: sequence s, KV head g, tokens [tok0, tok1) of
+  // the current chunk (at most part_tokens of them).
+  int s = 0, g = 0, tok0 = 0, tok1 = 0, npass = 0;
+  int64_t head0 = 0;  // first query row of (s, g)
   int lane_block = 0;
-  if constexpr (PAGED) {
-    const int b0 = tok0 >> p.log2_block;
-    const int nb = ((tok1 - 1) >> p.log2_block) - b0 + 1;
-    if (lane < nb) {
-      const int id = p.tables[int64_t(s) * p.max_blocks + b0 + lane];
-      lane_block = min(max(id, 0), p.num_blocks - 1);
-    }
-  }
+
+  // Running state over the chunks of a range: lane i keeps, for head i % G,
+  // the running max and weight sum.  acc holds each lane's rows' share of the
+  // current chunk's weighted V sums; with the balanced schedule a range may
+  // take several chunks, and the running sums of the earlier ones wait in
+  // LDS (head h at keep + h * D).
+  float acc[G * NV];  // [head][value]; after a chunk's reduction, PER sums per lane
+  float run_m = -INFINITY, run_l = 0.f;
+  // After the reduction lane (r, c) holds sums [r PER, (r + 1) PER) of the
+  // flattened (head, value) index: head my_h, values e0 .. e0 + PER - 1 at
+  // position c, i.e. PER / RUN runs of RUN consecutive elements of the row.
+  constexpr int PER = G * NV / 8;
+  constexpr int RUN = PER < EPC ? PER : EPC;
+  int my_h = r * PER / NV;
+  int e0 = r * PER % NV;
+  auto refresh_lane = [&]() {
+    const int l = opaque(lane_id);
+    lane = l;
+    r = l >> 3;
+    c = l & 7;
+    m = l & 15;
+    q4 = l >> 4;
+    my_h = r * PER / NV;
+    e0 = r * PER % NV;
+  };
+  auto elem = [&](int q) {  // row element of held sum q
+    const int e = e0 + q;
+    return (e / EPC) * (128 / T::bytes) + c * EPC + e % EPC;
+  };
+  float* const keep = lds + lds_rows(p.part_tokens) * G + kWave;
 
   // First row of pass `pass` (clamped to the last real pass, so padding
   // passes re-read cached rows) and how many of its 8 rows are in the context.
@@ -331,19 +468,18 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
     }
   };
 
-  // ---- pass 1: scores, scaled to the log2 domain, into LDS ----------------
-  float run_max = -INFINITY;
-  uint4 bufA[U][NCH], bufB[U][NCH];
-  if constexpr (MFMA) {
-    // Lane (m = lane % 16, q4 = lane / 16) holds, of token m of a 16-token
-    // tile, elements [32 kk + 8 q4, +8) for step kk -- the A layout of
-    // v_mfma_f32_16x16x32 -- and of query head m the same elements as the B
-    // operand (zero for m >= G).  The result D[4 q4 + i][m] is the score of
-    // token 4 q4 + i for head m.
-    const int m = lane & 15;
-    const int q4 = lane >> 4;
-    uint4 qb[KK];
-    {
+  // Query registers of the current (s, g).
+  // MFMA: lane (m = lane % 16, q4 = lane / 16) holds, of token m of a
+  // 16-token tile, elements [32 kk + 8 q4, +8) for step kk -- the A layout of
+  // v_mfma_f32_16x16x32 -- and of query head m the same elements as the B
+  // operand (zero for m >= G).  The result D[4 q4 + i][m] is the score of
+  // token 4 q4 + i for head m.
+  // Vector ALU: lane (r, c) holds chunks j * 128 + c * 16 of row r of each
+  // 8-row pass; the query chunks matching them stay in registers.
+  uint4 qb[MFMA ? KK : 1];
+  uint4 qc[MFMA ? 1 : G][NCH];
+  auto load_q = [&]() {
+    if constexpr (MFMA) {
       const char* qrow = reinterpret_cast<const char*>(p.q) + (head0 + min(m, G - 1)) * ROW_BYTES + q4 * 16;
       const uint32_t keep = m < G ? ~0u : 0u;
 #pragma unroll
@@ -351,72 +487,7 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
         uint4 v = *reinterpret_cast<const uint4*>(qrow + kk * 64);
         qb[kk] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
       }
-    }
-    // The two 8-row passes of a tile are consecutive rows of one block (or of
-    // the contiguous region), so one resource spans both.
-    auto load_tile = [&](uint4 (&kt)[KK], int tile) {
-      int live0, live1;
-      const char* rows0 = pass_rows(p.k, 2 * tile, live0);
-      pass_rows(p.k, 2 * tile + 1, live1);
-      const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
-      const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
-      const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
-    };
-    float* sink = lds + lds_rows(p.part_tokens) * G + lane;
-    auto score_tile = [&](const uint4 (&kt)[KK], int tile) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = mfma_qk(T{}, kt[kk], qb[kk], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = tile * 16 + q4 * 4 + i;
-        float sc = acc[i] * p.scale_log2e;
-        if (tok0 + row >= tok1 || m >= G) sc = -INFINITY;  // past the context, or a padding head
-        *(m < G ? lds + row * G + m : sink) = sc;
-        run_max = fmaxf(run_max, sc);
-      }
-    };
-    auto load_tiles = [&](uint4 (&kt)[KT][KK], int b) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t) load_tile(kt[t], b * KT + t);
-    };
-    auto score_tiles = [&](const uint4 (&kt)[KT][KK], int b) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t) score_tile(kt[t], b * KT + t);
-    };
-    const int npairs = (npass + 4 * KT - 1) / (4 * KT);  // pairs of K buffers
-    uint4 ktA[KT][KK], ktB[KT][KK];
-    load_tiles(ktA, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tiles(ktB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; i < npairs; ++i) {
-      score_tiles(ktA, 2 * i);
-      __builtin_amdgcn_sched_barrier(0);
-      load_tiles(ktA, 2 * i + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      score_tiles(ktB, 2 * i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_tiles(ktB, 2 * i + 3);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // first V rows start streaming while the weights are formed
-    load_buf(p.v, bufA, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_buf(p.v, bufB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // head m's scores sit in lanes m, m+16, m+32, m+48; leave each lane i
-    // with the max of head i % G, as the vector-ALU path does
-    run_max = fmaxf(run_max, __shfl_xor(run_max, 16));
-    run_max = fmaxf(run_max, __shfl_xor(run_max, 32));
-    run_max = __shfl(run_max, lane % G);
-  } else {
-    // Lane (r, c) holds chunks j * 128 + c * 16 of row r of each 8-row pass;
-    // the query chunks matching them stay in registers.
-    uint4 qc[G][NCH];
-    {
+    } else {
       const char* qrow = reinterpret_cast<const char*>(p.q) + head0 * ROW_BYTES + c * 16;
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -424,203 +495,447 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(DecodeParams p)
         for (int j = 0; j < NCH; ++j)
           qc[h][j] = *reinterpret_cast<const uint4*>(qrow + h * ROW_BYTES + j * 128);
     }
-    auto score_buf = [&](const uint4 (&buf)[U][NCH], int b) {
+  };
+
+  auto begin_range = [&]() {
+    head0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
+    run_m = -INFINITY;
+    run_l = 0.f;
+  };
+
+  // Reduces tokens [tok0, tok1) into the running state; `first` and `last`
+  // say where the chunk sits in its range.
+  auto chunk = [&](bool first, bool last) {
+    refresh_lane();
+    npass = (tok1 - tok0 + kRowsPerPass - 1) / kRowsPerPass;
+    // Per chunk, so the query registers are free during the V pass; the
+    // compiler barrier keeps the loads (invariant over a range) from being
+    // hoisted out of the chunk loop, which would pin them through it.
+    asm volatile("" ::: "memory");
+    load_q();
+    // Physical ids of this chunk's blocks, one per lane (clamped into the
+    // pool so a corrupt table cannot read outside the caches).
+    if constexpr (PAGED) {
+      const int b0 = tok0 >> p.log2_block;
+      const int nb = ((tok1 - 1) >> p.log2_block) - b0 + 1;
+      lane_block = 0;
+      if (lane < nb) {
+        const int id = p.tables[int64_t(s) * p.max_blocks + b0 + lane];
+        lane_block = min(max(id, 0), p.num_blocks - 1);
+      }
+    }
+    __syncthreads();  // the previous chunk's weights have all been read
+
+    // ---- pass 1: scores, scaled to the log2 domain, into LDS --------------
+    float cmax = -INFINITY;
+    uint4 bufA[U][NCH], bufB[U][NCH];
+    if constexpr (MFMA) {
+      // The two 8-row passes of a tile are consecutive rows of one block (or
+      // of the contiguous region), so one resource spans both.
+      auto load_tile = [&](uint4 (&kt)[KK], int tile) {
+        int live0, live1;
+        const char* rows0 = pass_rows(p.k, 2 * tile, live0);
+        pass_rows(p.k, 2 * tile + 1, live1);
+        const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
+        const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
+        const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
+      };
+      float* sink = lds + lds_rows(p.part_tokens) * G + lane;
+      auto score_tile = [&](const uint4 (&kt)[KK], int tile) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk(T{}, kt[kk], qb[kk], sacc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = tile * 16 + q4 * 4 + i;
+          float sc = sacc[i] * p.scale_log2e;
+          if (tok0 + row >= tok1 || m >= G) sc = -INFINITY;  // past the context, or a padding head
+          *(m < G ? lds + row * G + m : sink) = sc;
+          cmax = fmaxf(cmax, sc);
+        }
+      };
+      auto load_tiles = [&](uint4 (&kt)[KT][KK], int b) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t) load_tile(kt[t], b * KT + t);
+      };
+      auto score_tiles = [&](const uint4 (&kt)[KT][KK], int b) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t) score_tile(kt[t], b * KT + t);
+      };
+      const int npairs = (npass + 4 * KT - 1) / (4 * KT);  // pairs of K buffers
+      uint4 ktA[KT][KK], ktB[KT][KK];
+      load_tiles(ktA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tiles(ktB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < npairs; ++i) {
+        score_tiles(ktA, 2 * i);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tiles(ktA, 2 * i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        score_tiles(ktB, 2 * i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tiles(ktB, 2 * i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // first V rows start streaming while the weights are formed
+      load_buf(p.v, bufA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_buf(p.v, bufB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // head m's scores sit in lanes m, m+16, m+32, m+48; leave each lane i
+      // with the max of head i % G, as the vector-ALU path does
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = __shfl(cmax, lane % G);
+    } else {
+      auto score_buf = [&](const uint4 (&buf)[U][NCH], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pass = b * U + u;
+          float sc[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, buf[u][j], qc[h][j], a);
+            sc[h] = row8_sum(a);
+          }
+          float mine = sc[0];
+#pragma unroll
+          for (int h = 1; h < G; ++h) mine = (c % G == h) ? sc[h] : mine;
+          mine *= p.scale_log2e;
+          if (tok0 + pass * kRowsPerPass + r >= tok1) mine = -INFINITY;  // past the context
+          // lanes c and c + G hold the same head: both store the same value
+          lds[(pass * kRowsPerPass + r) * G + c % G] = mine;
+          cmax = fmaxf(cmax, mine);
+        }
+      };
+      const int npairs = (npass + 2 * U - 1) / (2 * U);
+      load_buf(p.k, bufA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_buf(p.k, bufB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // The scheduling barriers keep the order "consume one buffer, refill it,
+      // consume the other, refill it", so one buffer is always in flight.
+      for (int i = 0; i < npairs; ++i) {
+        score_buf(bufA, 2 * i);
+        __builtin_amdgcn_sched_barrier(0);
+        load_buf(p.k, bufA, 2 * i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        score_buf(bufB, 2 * i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_buf(p.k, bufB, 2 * i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // first V rows start streaming while the weights are formed
+      load_buf(p.v, bufA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_buf(p.v, bufB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // lane i's cmax belongs to head i % G: reduce over that head's lanes
+#pragma unroll
+      for (int mm = G; mm < kWave; mm <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, mm));
+    }
+
+    // ---- softmax weights against the running max ---------------------------
+    // The V pass runs whole pairs of 2U passes; the score pass wrote whole
+    // pairs of 16-token tiles (MFMA) or the same 2U-pass pairs.  Rows the V
+    // pass reaches beyond the written scores are padding and get weight 0.
+    const float new_m = fmaxf(run_m, cmax);
+    const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
+    const int rows_k = MFMA ? (npass + 4 * KT - 1) / (4 * KT) * (32 * KT) : npass_v * kRowsPerPass;
+    __syncthreads();
+    float wsum = 0.f;
+    const int nent = npass_v * kRowsPerPass * G;
+    const int nent_k = rows_k * G;
+    for (int e = lane; e < nent; e += kWave) {  // entry e belongs to head e % G = lane % G
+      const float w = e < nent_k ? __builtin_amdgcn_exp2f(lds[e] - new_m) : 0.f;
+      lds[e] = w;
+      wsum += w;
+    }
+#pragma unroll
+    for (int mm = G; mm < kWave; mm <<= 1) wsum += __shfl_xor(wsum, mm);
+    // Earlier chunks were weighted against run_m: their sums scale by f
+    // (0 on the first chunk, whose running sum is 0).
+    const float f = __builtin_amdgcn_exp2f(run_m - new_m);
+    run_l = run_l * f + wsum;
+    run_m = new_m;
+    __syncthreads();
+
+    // ---- pass 2: weighted sum of V ------------------------------------------
+    auto accumulate_buf = [&](const uint4 (&buf)[U][NCH], int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int pass = b * U + u;
-        float sc[G];
+        const float* wrow = lds + (pass * kRowsPerPass + r) * G;
+        float w[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float a = 0.f;
+        for (int h = 0; h < G; ++h) w[h] = wrow[h];
 #pragma unroll
-          for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, buf[u][j], qc[h][j], a);
-          sc[h] = row8_sum(a);
+        for (int j = 0; j < NCH; ++j) {
+          float vv[EPC];
+          widen(T{}, buf[u][j], vv);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h * NV + j * EPC + e] = fmaf(w[h], vv[e], acc[h * NV + j * EPC + e]);
         }
-        float mine = sc[0];
-#pragma unroll
-        for (int h = 1; h < G; ++h) mine = (c % G == h) ? sc[h] : mine;
-        mine *= p.scale_log2e;
-        if (tok0 + pass * kRowsPerPass + r >= tok1) mine = -INFINITY;  // past the context
-        // lanes c and c + G hold the same head: both store the same value
-        lds[(pass * kRowsPerPass + r) * G + c % G] = mine;
-        run_max = fmaxf(run_max, mine);
       }
     };
-    const int npairs = (npass + 2 * U - 1) / (2 * U);
-    load_buf(p.k, bufA, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_buf(p.k, bufB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // The scheduling barriers keep the order "consume one buffer, refill it,
-    // consume the other, refill it", so one buffer is always in flight.
-    for (int i = 0; i < npairs; ++i) {
-      score_buf(bufA, 2 * i);
+#pragma unroll
+    for (int i = 0; i < G * NV; ++i) acc[i] = 0.f;
+    const int npairs_v = npass_v / (2 * U);
+    for (int i = 0; i < npairs_v; ++i) {
+      accumulate_buf(bufA, 2 * i);
       __builtin_amdgcn_sched_barrier(0);
-      load_buf(p.k, bufA, 2 * i + 2);
+      load_buf(p.v, bufA, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      score_buf(bufB, 2 * i + 1);
+      accumulate_buf(bufB, 2 * i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_buf(p.k, bufB, 2 * i + 3);
+      load_buf(p.v, bufB, 2 * i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // first V rows start streaming while the weights are formed
-    load_buf(p.v, bufA, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_buf(p.v, bufB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // lane i's run_max belongs to head i % G: reduce over that head's lanes
-#pragma unroll
-    for (int mm = G; mm < kWave; mm <<= 1) run_max = fmaxf(run_max, __shfl_xor(run_max, mm));
-  }
 
-  // ---- softmax weights -----------------------------------------------------
-  // The V pass runs whole pairs of 2U passes; the score pass wrote whole
-  // pairs of 16-token tiles (MFMA) or the same 2U-pass pairs.  Rows the V pass
-  // reaches beyond the written scores are padding and get weight 0.
-  const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
-  const int rows_k = MFMA ? (npass + 4 * KT - 1) / (4 * KT) * (32 * KT) : npass_v * kRowsPerPass;
-  __syncthreads();
-  float wsum = 0.f;
-  const int nent = npass_v * kRowsPerPass * G;
-  const int nent_k = rows_k * G;
-  for (int e = lane; e < nent; e += kWave) {  // entry e belongs to head e % G = lane % G
-    const float w = e < nent_k ? __builtin_amdgcn_exp2f(lds[e] - run_max) : 0.f;
-    lds[e] = w;
-    wsum += w;
-  }
-#pragma unroll
-  for (int mm = G; mm < kWave; mm <<= 1) wsum += __shfl_xor(wsum, mm);
-  __syncthreads();
+    reduce_scatter8(acc, lane);
 
-  // ---- pass 2: weighted sum of V --------------------------------------------
-  float acc[G][NV];
+    // Several chunks: the running sums of the earlier ones wait in LDS,
+    // head h's at keep + h * D (every lane its own words).
+    if constexpr (BAL) {
+      if (!first) {
+        const float fh = __shfl(f, my_h);  // lane h holds head h's factor
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+        for (int q = 0; q < PER; ++q) acc[q] = fmaf(keep[my_h * D + elem(q)], fh, acc[q]);
+      }
+      if (!last) {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) acc[h][e] = 0.f;
-  auto accumulate_buf = [&](const uint4 (&buf)[U][NCH], int b) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pass = b * U + u;
-      const float* wrow = lds + (pass * kRowsPerPass + r) * G;
-      float w[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) w[h] = wrow[h];
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        float vv[EPC];
-        widen(T{}, buf[u][j], vv);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][j * EPC + e] = fmaf(w[h], vv[e], acc[h][j * EPC + e]);
+        for (int q = 0; q < PER; q += RUN) store_run<RUN>(keep + my_h * D + elem(q), acc + q, 1.f);
       }
     }
   };
-  const int npairs_v = npass_v / (2 * U);
-  for (int i = 0; i < npairs_v; ++i) {
-    accumulate_buf(bufA, 2 * i);
-    __builtin_amdgcn_sched_barrier(0);
-    load_buf(p.v, bufA, 2 * i + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate_buf(bufB, 2 * i + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_buf(p.v, bufB, 2 * i + 3);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
-  // Sum the 8 row lanes sharing chunk position c (lanes c, c+8, ..., c+56).
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      float x = acc[h][e];
-      x += dpp<kRowRor8>(x);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[h][e] = x;
-    }
-
-  // Lane h (h < G) holds head h's max and weight sum.
-  float head_l[G], head_m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    head_l[h] = __shfl(wsum, h);
-    head_m[h] = __shfl(run_max, h);
-  }
-
-  if (nparts_seq == 1) {
-    // Lane (r, c) writes head r's values at its chunk positions.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (r != h) continue;
-      const float inv = 1.f / head_l[h];
-      const int64_t row = head0 + h;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int d0 = j * (128 / T::bytes) + c * EPC;
-        const float* a = &acc[h][j * EPC];
-        if (p.out_f32 || T::bytes == 4) {
-          float* o = reinterpret_cast<float*>(p.out) + row * D + d0;
-#pragma unroll
-          for (int e = 0; e < EPC; e += 4)
-            *reinterpret_cast<float4*>(o + e) =
-                make_float4(a[e] * inv, a[e + 1] * inv, a[e + 2] * inv, a[e + 3] * inv);
-        } else {
-          store_narrow(T{}, reinterpret_cast<uint16_t*>(p.out) + row * D + d0, a, inv);
-        }
+  // Reduces tokens [from, to) of (s, g) chunk by chunk.
+  auto reduce_range = [&](int from, int to) {
+    begin_range();
+    if constexpr (!BAL) {  // a partition is one chunk
+      tok0 = from;
+      tok1 = to;
+      chunk(true, true);
+    } else {
+      for (int t = from; t < to; t += p.part_tokens) {
+        tok0 = t;
+        tok1 = min(t + p.part_tokens, to);
+        chunk(t == from, tok1 == to);
       }
     }
-    return;
-  }
+  };
 
-  // Several partitions: publish this one's (m, l, o) for decode_combine_kernel.
+  // Finishes the range: the group's normalised output rows when the range is
+  // the whole context, else one (max, sum, weighted sum) record per head at
+  // rows rec0 + h * rec_stride of the workspace.
+  auto finish = [&](bool whole, int64_t rec0, int64_t rec_stride) {
+    refresh_lane();
+    const float my_l = __shfl(run_l, my_h);  // lane h holds head h's max and sum
+    const float my_m = __shfl(run_m, my_h);
+    if (whole) {
+      const float inv = 1.f / my_l;
+      const int64_t row = (head0 + my_h) * D;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (r != h) continue;
-    const int64_t prow = (head0 + h) * p.num_parts + part;
-    float* o = p.part_o + prow * D;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int d0 = j * (128 / T::bytes) + c * EPC;
-#pragma unroll
-      for (int e = 0; e < EPC; e += 4)
-        *reinterpret_cast<float4*>(o + d0 + e) =
-            make_float4(acc[h][j * EPC + e], acc[h][j * EPC + e + 1], acc[h][j * EPC + e + 2],
-                        acc[h][j * EPC + e + 3]);
+      for (int q = 0; q < PER; q += RUN) {
+        float* of = reinterpret_cast<float*>(p.out) + row + elem(q);
+        if constexpr (T::bytes == 4) {
+          store_run<RUN>(of, acc + q, inv);
+        } else {
+          if (p.out_f32) store_run<RUN>(of, acc + q, inv);
+          else store_run<T, RUN>(T{}, reinterpret_cast<uint16_t*>(p.out) + row + elem(q), acc + q, inv);
+        }
+      }
+      return;
     }
-    if (c == 0) {
-      p.part_ml[prow * 2 + 0] = head_m[h];
-      p.part_ml[prow * 2 + 1] = head_l[h];
+    const int64_t prow = rec0 + my_h * rec_stride;
+#pragma unroll
+    for (int q = 0; q < PER; q += RUN) store_run<RUN>(p.part_o + prow * D + elem(q), acc + q, 1.f);
+    if (c == 0 && e0 == 0) {  // one lane per head
+      p.part_ml[prow * 2 + 0] = my_m;
+      p.part_ml[prow * 2 + 1] = my_l;
+    }
+  };
+
+  if constexpr (!BAL) {
+    const Unit unit = unit_of(blockIdx.x, p);
+    g = unit.g;
+    s = unit.s;
+    const int part = unit.part;
+    const int ctx = min(p.ctx_lens[s], p.max_ctx);
+    if (ctx <= 0) {
+      // no context: defined as a zero output row
+      if (part == 0) {
+        const int64_t h0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
+        for (int i = lane; i < G * D; i += kWave) {
+          if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[h0 * D + i] = 0.f;
+          else reinterpret_cast<uint16_t*>(p.out)[h0 * D + i] = 0;
+        }
+      }
+      return;
+    }
+    const int from = part * p.part_tokens;
+    if (from >= ctx) return;
+    const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
+    reduce_range(from, min(from + p.part_tokens, ctx));
+    finish(nparts_seq == 1, head0 * p.num_parts + part, p.num_parts);
+  } else {
+    const Sched sc = *p.sched;
+    const int k = piece_of_workgroup(blockIdx.x, sc);
+    if (k < 0) return;
+    const int64_t first = piece_start(k, sc);
+    const int64_t end = piece_start(k + 1, sc);
+    int64_t pos = first;
+    g = int(pos / sc.tiles_per_head);
+    s = p.start_seq[k];
+    for (;;) {
+      const int c0 = p.cum[s];
+      const int n = p.cum[s + 1] - c0;
+      const int64_t seg = int64_t(g) * sc.tiles_per_head + c0;  // first tile of (s, g)
+      const int t0 = int(pos - seg);
+      const int t1 = int(min(end - seg, int64_t(n)));
+      const int ctx = min(p.ctx_lens[s], p.max_ctx);
+      reduce_range(t0 * kTile, min(t1 * kTile, ctx));
+      // A cut range is this piece's first (it holds piece_start(k)) or its last.
+      const int64_t slot = 2 * int64_t(k) + (pos == first ? 0 : 1);
+      finish(t0 == 0 && t1 == n, slot * G, 1);
+      pos = seg + t1;
+      if (pos >= end) break;
+      do {  // next sequence with a context (one exists: pos < end <= total)
+        if (++s == p.num_seqs) {
+          s = 0;
+          ++g;
+        }
+      } while (p.cum[s + 1] == p.cum[s]);
     }
   }
 }
 
-// Merges the partitions of each (sequence, query head):
+// Builds the balanced schedule in the workspace: cum[s] = tiles of sequences
+// before s (per KV head), the header, and start_seq[k] = the sequence that
+// holds piece k's first tile.  One workgroup.
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams p) {
+  __shared__ int wave_sums[kPlanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int S = p.num_seqs;
+  int carry = 0;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < S) {
+      const int ctx = min(p.ctx_lens[s], p.max_ctx);
+      n = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
+    }
+    int x = n;  // inclusive scan over the workgroup
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kPlanThreads / kWave; ++w) {
+      before += w < wave ? wave_sums[w] : 0;
+      total += wave_sums[w];
+    }
+    if (s < S) p.cum[s] = carry + before + x - n;
+    carry += total;
+    __syncthreads();  // wave_sums is reused
+  }
+  const int T = carry;
+  Sched sc;
+  sc.tiles_per_head = T;
+  sc.total = int64_t(p.num_kv_heads) * T;
+  sc.pieces = int(min(int64_t(p.num_waves), sc.total / kMinTilesPerPiece));
+  if (sc.total > 0 && sc.pieces == 0) sc.pieces = 1;
+  if (tid == 0) {
+    p.cum[S] = T;
+    *p.sched = sc;
+  }
+  __syncthreads();  // cum complete
+  if (sc.pieces == 0) return;
+  // Pieces whose first tile lies in (s, g): k in [piece_of(A - 1) + 1, piece_of(B - 1)].
+  const int64_t nseg = int64_t(p.num_kv_heads) * S;
+  for (int64_t idx = tid; idx < nseg; idx += kPlanThreads) {
+    const int g = int(idx / S), s = int(idx % S);
+    const int c0 = p.cum[s], c1 = p.cum[s + 1];
+    if (c1 == c0) continue;
+    const int64_t A = int64_t(g) * T + c0, B = int64_t(g) * T + c1;
+    const int64_t k0 = A == 0 ? 0 : piece_of(A - 1, sc) + 1;
+    const int64_t k1 = piece_of(B - 1, sc);
+    for (int64_t k = k0; k <= k1; ++k) p.start_seq[k] = s;
+  }
+}
+
+// Merges the records of each (sequence, query head):
 //   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),  out = sum_i 2^(m_i - M) o_i / L.
-// One wave per (sequence, query head).  Lane i holds partition i's (m, l)
-// (64 partitions per round), so the max and the sum are wave reductions; each
-// lane then owns D / 64 output elements and adds the partitions in index
-// order, so the result never depends on the order in which partitions
-// finished.  Every load address is known up front, so the loads of a round are
-// all in flight together.
-template <class T, int D>
+// One wave per (sequence, query head).  Lane i holds record i's (m, l)
+// (64 records per round), so the max and the sum are wave reductions; each
+// lane then owns D / 64 output elements and adds the records in token order,
+// so the result never depends on the order in which the records were written.
+// Every load address is known up front, so the loads of a round are all in
+// flight together.
+//   fixed partitions: record i = partition i, rows (head * num_parts + i);
+//   balanced: the pieces k_lo..k_hi that cut the range, row (slot * G + h)
+//   with slot 2 k_lo + (range starts inside piece k_lo), then 2 k; a range
+//   inside one piece was written whole, and an empty context gives zeros.
+template <class T, int D, bool BAL>
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   const int64_t head = blockIdx.x;  // s * Hq + query head
   const int s = int(head / p.num_q_heads);
   const int lane = threadIdx.x;
   const int ctx = min(p.ctx_lens[s], p.max_ctx);
-  if (ctx <= 0) return;
-  const int np = (ctx + p.part_tokens - 1) / p.part_tokens;
-  if (np <= 1) return;  // the partition kernel wrote this output itself
   constexpr int PER = D / kWave;  // output values per lane
-  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + head * p.num_parts;
-  const float* po = p.part_o + head * p.num_parts * D + lane * PER;
+  const int64_t obase = head * D + lane * PER;
+  int np;
+  int64_t rec0 = 0, stride = 1, first_rec = 0;
+  if constexpr (!BAL) {
+    if (ctx <= 0) return;  // the partition kernel wrote the zero row
+    np = (ctx + p.part_tokens - 1) / p.part_tokens;
+    if (np <= 1) return;  // the partition kernel wrote this output itself
+    rec0 = first_rec = head * p.num_parts;
+    stride = 1;
+  } else {
+    if (ctx <= 0) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[obase + k] = 0.f;
+        else reinterpret_cast<uint16_t*>(p.out)[obase + k] = 0;
+      }
+      return;
+    }
+    const Sched sc = *p.sched;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int qh = int(head % p.num_q_heads);
+    const int g = qh / G, hl = qh % G;
+    const int c0 = p.cum[s], c1 = p.cum[s + 1];
+    const int64_t A = int64_t(g) * sc.tiles_per_head + c0;
+    const int64_t B = int64_t(g) * sc.tiles_per_head + c1;
+    const int64_t klo = piece_of(A, sc), khi = piece_of(B - 1, sc);
+    if (klo == khi) return;  // written whole by the decode kernel
+    np = int(khi - klo + 1);
+    // record i (i >= 1) sits at slot 2 (klo + i): rows (2 (klo + i)) G + hl
+    rec0 = 2 * klo * G + hl;
+    stride = 2 * G;
+    first_rec = (2 * klo + (A == piece_start(klo, sc) ? 0 : 1)) * G + hl;
+  }
+  auto rec = [&](int i) -> int64_t { return i == 0 ? first_rec : rec0 + int64_t(i) * stride; };
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml);
+  const float* po = p.part_o + lane * PER;
 
   float M = -INFINITY;
-  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[i].x);
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[rec(i)].x);
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+  for (int mm = 1; mm < kWave; mm <<= 1) M = fmaxf(M, __shfl_xor(M, mm));
 
   float L = 0.f;
   float o[PER];
@@ -628,7 +943,7 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   for (int base = 0; base < np; base += kWave) {
     const int n = min(np - base, kWave);
-    const float2 mine = lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.f);
+    const float2 mine = lane < n ? ml[rec(base + lane)] : make_float2(-INFINITY, 0.f);
     const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past n
     L += mine.y * f;
     int i = 0;
@@ -637,7 +952,7 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int k = 0; k < PER; ++k) x[u][k] = po[int64_t(base + i + u) * D + k];
+        for (int k = 0; k < PER; ++k) x[u][k] = po[rec(base + i + u) * D + k];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float fu = __shfl(f, i + u);
@@ -648,13 +963,12 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
     for (; i < n; ++i) {
       const float fu = __shfl(f, i);
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, po[int64_t(base + i) * D + k], o[k]);
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, po[rec(base + i) * D + k], o[k]);
     }
   }
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m);
+  for (int mm = 1; mm < kWave; mm <<= 1) L += __shfl_xor(L, mm);
   const float inv = 1.f / L;
-  const int64_t obase = head * D + lane * PER;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const float x = o[k] * inv;
@@ -676,12 +990,13 @@ int log2_exact(int x) {
 }
 
 struct Plan {
-  int part_tokens = 0;
-  int num_parts = 0;
+  bool balanced = false;
+  int part_tokens = 0;   // fixed: partition length; balanced: chunk length
+  int num_parts = 0;     // fixed only
   int max_ctx = 0;
+  int max_pieces = 0;    // balanced: pieces the workspace has room for
   size_t workspace = 0;
-  size_t part_o_bytes = 0;
-  size_t part_ml_bytes = 0;
+  size_t part_o_off = 0, part_ml_off = 0, sched_off = 0, cum_off = 0, start_off = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -699,6 +1014,34 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   if (D != 64 && D != 128) return fail(PA_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (!std::isfinite(scale)) return fail(PA_E_INVAL, "scale must be finite");
   if (ctx_bound <= 0) return fail(PA_E_INVAL, "context bound must be positive");
+  if (int64_t(S) * Hq > INT32_MAX) return fail(PA_E_UNSUPPORTED, "too many (sequence, head) rows");
+  plan->max_ctx = ctx_bound;
+  plan->workspace = 0;
+  if (partition == kBalanced) {
+    // Balanced schedule; chunks of kBalancedChunk tokens (a multiple of 16,
+    // so of every block size up to 16, and at most 64 blocks of 8 tokens).
+    plan->balanced = true;
+    plan->part_tokens = kBalancedChunk;
+    const int64_t tiles = (int64_t(ctx_bound) + kTile - 1) / kTile;
+    if (int64_t(S) * tiles > INT32_MAX) return fail(PA_E_UNSUPPORTED, "num_seqs * max_ctx too large");
+    const int64_t bound = int64_t(S) * Hkv * tiles / kMinTilesPerPiece;
+    plan->max_pieces = int(std::max<int64_t>(1, std::min<int64_t>(bound, kMaxWaves)));
+    if (S == 0) return ok();
+    size_t off = 0;
+    plan->sched_off = off;
+    off += align256(sizeof(Sched));
+    plan->cum_off = off;
+    off += align256(size_t(S + 1) * sizeof(int32_t));
+    plan->start_off = off;
+    off += align256(size_t(plan->max_pieces) * sizeof(int32_t));
+    const size_t recs = size_t(2) * plan->max_pieces * G;  // two records per piece and head
+    plan->part_ml_off = off;
+    off += align256(recs * 2 * sizeof(float));
+    plan->part_o_off = off;
+    off += align256(recs * D * sizeof(float));
+    plan->workspace = off;
+    return ok();
+  }
   const int unit = block > 8 ? block : 8;
   const int cap = block > 0 ? (64 * block < kMaxPartition ? 64 * block : kMaxPartition) : kMaxPartition;
   int pt = partition;
@@ -715,55 +1058,122 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   if (pt <= 0 || pt % unit || pt > cap)
     return fail(PA_E_INVAL, "partition_size must be a multiple of 8 and of block_size, at most " +
                                 std::to_string(cap));
+  plan->balanced = false;
   plan->part_tokens = pt;
-  plan->max_ctx = ctx_bound;
   plan->num_parts = (ctx_bound + pt - 1) / pt;
-  if (int64_t(plan->num_parts) * (int64_t(S) + kSeqChunk) * Hkv > INT32_MAX || int64_t(S) * Hq > INT32_MAX)
+  if (int64_t(plan->num_parts) * (int64_t(S) + kSeqChunk) * Hkv > INT32_MAX)
     return fail(PA_E_UNSUPPORTED, "too many (partition, sequence, head) units for one launch");
-  plan->workspace = 0;
   if (plan->num_parts > 1 && S > 0) {
     const size_t rows = size_t(S) * Hq * plan->num_parts;
-    plan->part_o_bytes = align256(rows * D * sizeof(float));
-    plan->part_ml_bytes = align256(rows * 2 * sizeof(float));
-    plan->workspace = plan->part_o_bytes + plan->part_ml_bytes;
+    plan->part_o_off = 0;
+    plan->part_ml_off = align256(rows * D * sizeof(float));
+    plan->workspace = plan->part_ml_off + align256(rows * 2 * sizeof(float));
   }
   return ok();
 }
 
-template <class T, int D, int G, bool PAGED>
-void launch_one(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  const size_t lds = size_t(lds_floats<G>(p.part_tokens)) * sizeof(float);
+// Points the parameter block at the workspace regions of the plan.
+void bind_workspace(const Plan& plan, void* ws, DecodeParams* p) {
+  char* base = static_cast<char*>(ws);
+  p->part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+  p->part_ml = reinterpret_cast<float*>(base + plan.part_ml_off);
+  p->sched = reinterpret_cast<Sched*>(base + plan.sched_off);
+  p->cum = reinterpret_cast<int32_t*>(base + plan.cum_off);
+  p->start_seq = reinterpret_cast<int32_t*>(base + plan.start_off);
+}
+
+template <class T, int D, int G, bool PAGED, bool MFMA>
+int occupancy(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, D, G, PAGED, MFMA, true>, kWave, lds) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+// Waves of the balanced decode kernel the current GPU holds at once: CUs x
+// resident waves per CU, the smaller over the kernel's variants (paged or
+// contiguous, matrix-core or vector scores) so that all of them cut the work
+// identically; a multiple of 8 in [8, kMaxWaves].  Cached per device.
+std::atomic<int> g_waves_override{0};  // pa_decode_set_waves; 0 = automatic
+
+template <class T, int D, int G>
+int balanced_waves() {
+  const int forced = g_waves_override.load(std::memory_order_relaxed);
+  if (forced > 0) return forced;
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  const size_t lds = size_t(lds_floats_balanced<G, D>()) * sizeof(float);
+  int occ = std::min(occupancy<T, D, G, true, false>(lds), occupancy<T, D, G, false, false>(lds));
+  if constexpr (mfma_capable<T, G>())
+    occ = std::min(occ, std::min(occupancy<T, D, G, true, true>(lds), occupancy<T, D, G, false, true>(lds)));
+  if (occ <= 0) return 0;
+  const int waves = std::max(8, std::min(kMaxWaves, cus * occ) / 8 * 8);
+  cache[dev] = waves;
+  return waves;
+}
+
+template <class T, int D, int G, bool PAGED, bool BAL>
+void launch_decode(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  const size_t lds = size_t(BAL ? lds_floats_balanced<G, D>() : lds_floats<G>(p.part_tokens)) * sizeof(float);
   if constexpr (mfma_capable<T, G>()) {
     if (!PAGED || p.block_size >= 16) {
-      hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PAGED, true>), grid, dim3(kWave), lds, st, p);
+      hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, true, BAL>), grid, dim3(kWave), lds, st, p);
       return;
     }
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PAGED, false>), grid, dim3(kWave), lds, st, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, false, BAL>), grid, dim3(kWave), lds, st, p);
 }
 
-template <class T, int D, bool PAGED>
-pa_status launch_g(const DecodeParams& p, int G, int S, int Hkv, hipStream_t st) {
-  const int64_t seqs_padded = (int64_t(S) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
-  const dim3 grid(unsigned(int64_t(p.num_parts) * seqs_padded * Hkv));
-  switch (G) {
-    case 1: launch_one<T, D, 1, PAGED>(p, grid, st); break;
-    case 2: launch_one<T, D, 2, PAGED>(p, grid, st); break;
-    case 4: launch_one<T, D, 4, PAGED>(p, grid, st); break;
-    case 8: launch_one<T, D, 8, PAGED>(p, grid, st); break;
+template <class T, int D, int G, bool PAGED>
+pa_status launch_group(DecodeParams p, const Plan& plan, int S, int Hkv, hipStream_t st) {
+  const dim3 combine_grid(unsigned(int64_t(S) * p.num_q_heads));
+  if (!plan.balanced) {
+    const int64_t seqs_padded = (int64_t(S) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
+    launch_decode<T, D, G, PAGED, false>(p, dim3(unsigned(int64_t(p.num_parts) * seqs_padded * Hkv)), st);
+    pa_status ps = launch_status("decode partition kernel");
+    if (ps != PA_OK || p.num_parts <= 1) return ps;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, false>), combine_grid, dim3(kWave), 0, st, p);
+    return launch_status("decode combine kernel");
   }
-  pa_status ps = launch_status("decode partition kernel");
-  if (ps != PA_OK || p.num_parts <= 1) return ps;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(unsigned(int64_t(S) * p.num_q_heads)), dim3(kWave),
-                     0, st, p);
+  const int waves = balanced_waves<T, D, G>();
+  if (waves <= 0) return fail(PA_E_HIP, "could not size the balanced decode grid for this GPU");
+  p.num_waves = std::min(waves, plan.max_pieces);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
+  pa_status ps = launch_status("decode plan kernel");
+  if (ps != PA_OK) return ps;
+  launch_decode<T, D, G, PAGED, true>(p, dim3(unsigned((p.num_waves + 7) / 8 * 8)), st);
+  ps = launch_status("decode kernel");
+  if (ps != PA_OK) return ps;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, true>), combine_grid, dim3(kWave), 0, st, p);
   return launch_status("decode combine kernel");
 }
 
+template <class T, int D, bool PAGED>
+pa_status launch_g(const DecodeParams& p, const Plan& plan, int G, int S, int Hkv, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_group<T, D, 1, PAGED>(p, plan, S, Hkv, st);
+    case 2: return launch_group<T, D, 2, PAGED>(p, plan, S, Hkv, st);
+    case 4: return launch_group<T, D, 4, PAGED>(p, plan, S, Hkv, st);
+    default: return launch_group<T, D, 8, PAGED>(p, plan, S, Hkv, st);
+  }
+}
+
 template <bool PAGED>
-pa_status launch(const DecodeParams& p, pa_dtype kv, int D, int G, int S, int Hkv, hipStream_t st) {
-  if (kv == PA_F32) return D == 64 ? launch_g<F32, 64, PAGED>(p, G, S, Hkv, st) : launch_g<F32, 128, PAGED>(p, G, S, Hkv, st);
-  if (kv == PA_F16) return D == 64 ? launch_g<F16, 64, PAGED>(p, G, S, Hkv, st) : launch_g<F16, 128, PAGED>(p, G, S, Hkv, st);
-  return D == 64 ? launch_g<BF16, 64, PAGED>(p, G, S, Hkv, st) : launch_g<BF16, 128, PAGED>(p, G, S, Hkv, st);
+pa_status launch(const DecodeParams& p, const Plan& plan, pa_dtype kv, int D, int G, int S, int Hkv,
+                 hipStream_t st) {
+  if (kv == PA_F32)
+    return D == 64 ? launch_g<F32, 64, PAGED>(p, plan, G, S, Hkv, st) : launch_g<F32, 128, PAGED>(p, plan, G, S, Hkv, st);
+  if (kv == PA_F16)
+    return D == 64 ? launch_g<F16, 64, PAGED>(p, plan, G, S, Hkv, st) : launch_g<F16, 128, PAGED>(p, plan, G, S, Hkv, st);
+  return D == 64 ? launch_g<BF16, 64, PAGED>(p, plan, G, S, Hkv, st) : launch_g<BF16, 128, PAGED>(p, plan, G, S, Hkv, st);
 }
 
 pa_status check_paged(const pa_decode_args* a, Plan* plan) {
@@ -831,8 +1241,7 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   p.v = static_cast<const char*>(a->v_cache);
   p.tables = a->block_tables;
   p.ctx_lens = a->ctx_lens;
-  p.part_o = static_cast<float*>(a->workspace);
-  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.part_o_bytes);
+  bind_workspace(plan, a->workspace, &p);
   p.num_seqs = a->num_seqs;
   p.tile_bytes = int64_t(a->block_size) * a->head_dim * eb;
   p.region_bytes = 0;
@@ -847,7 +1256,7 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   p.num_parts = plan.num_parts;
   p.out_f32 = a->out_dtype == PA_F32;
   p.scale_log2e = a->scale * 1.4426950408889634f;
-  return launch<true>(p, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,
+  return launch<true>(p, plan, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,
                       a->num_kv_heads, static_cast<hipStream_t>(stream));
 }
 
@@ -876,8 +1285,7 @@ extern "C" pa_status pa_decode_contiguous(const pa_contig_args* a, pa_stream str
   p.v = static_cast<const char*>(a->v);
   p.tables = nullptr;
   p.ctx_lens = a->ctx_lens;
-  p.part_o = static_cast<float*>(a->workspace);
-  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan.part_o_bytes);
+  bind_workspace(plan, a->workspace, &p);
   p.num_seqs = a->num_seqs;
   p.tile_bytes = 0;
   p.region_bytes = int64_t(a->capacity) * a->head_dim * eb;
@@ -892,6 +1300,11 @@ extern "C" pa_status pa_decode_contiguous(const pa_contig_args* a, pa_stream str
   p.num_parts = plan.num_parts;
   p.out_f32 = a->out_dtype == PA_F32;
   p.scale_log2e = a->scale * 1.4426950408889634f;
-  return launch<false>(p, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,
+  return launch<false>(p, plan, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,
                        a->num_kv_heads, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_decode_set_waves(int32_t waves) {
+  const int w = waves <= 0 ? 0 : std::max(8, std::min(kMaxWaves, waves / 8 * 8));
+  return g_waves_override.exchange(w);
 }
