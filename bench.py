@@ -300,7 +300,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "kernel": "pa_decode (partition + combine launches)",
-                     "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg_bytes},
+                     "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg_bytes,
+                     "launch_ms_p10_median_p90": [round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)]},
         "cpu_baseline": None,
     }
     if comparison is not None:
