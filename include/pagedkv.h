@@ -267,6 +267,22 @@ pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_ou
 pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
 
 /*
+ * Debug check of pa_decode's device inputs.  The decode kernels clamp table
+ * entries into the pool rather than check them (a corrupt table gives a
+ * meaningless row, never an out-of-bounds read); this counts what a correct
+ * caller never passes: ctx_lens entries above the context bound (max_ctx, or
+ * max_blocks * block_size), and table entries j < ceil(ctx / block_size)
+ * outside [0, num_blocks).  The count goes to *count (device int32),
+ * asynchronously on stream.  Arguments are validated as for pa_decode
+ * (out, q and the caches are not read).
+ *
+ * With the environment variable PAGEDKV_DEBUG set (and not "0"), pa_decode
+ * runs this check first, synchronises the stream, and returns PA_E_INVAL
+ * without launching the decode when the count is not zero.
+ */
+pa_status pa_decode_validate(const pa_decode_args* args, int32_t* count, pa_stream stream);
+
+/*
  * The same attention on the contiguous layout the pages contrast paging with
  * ("Paged Attention", 定义: one region per sequence reserved for its maximum
  * length): K and V are [S][Hkv][capacity][head_dim]; no block table.  Used to

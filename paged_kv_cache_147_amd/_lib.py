@@ -92,6 +92,7 @@ _SIGS = {
     "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
     "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
     "pa_decode_set_waves": (c_i32, [c_i32]),
+    "pa_decode_validate": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp, c_vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -363,3 +364,18 @@ def pa_decode_set_waves(waves):
     """Waves the balanced schedule cuts the work into (0 = automatic); returns
     the previous setting."""
     return int(_lib.pa_decode_set_waves(int(waves)))
+
+
+def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, stream=None):
+    """Number of out-of-range context lengths and table entries (debug check;
+    synchronises the stream)."""
+    for t, dt in ((block_tables, torch.int32), (ctx_lens, torch.int32)):
+        if t.dtype != dt:
+            raise ValueError("block_tables and ctx_lens must be int32")
+    for t in (q, k_cache, v_cache, block_tables, ctx_lens):
+        _dev(t)
+    a = decode_args(None, q, k_cache, v_cache, block_tables, ctx_lens, 1.0, max_ctx, 0, None)
+    count = torch.empty(1, dtype=torch.int32, device=q.device)
+    s = stream if stream is not None else current_stream(q.device)
+    check(_lib.pa_decode_validate(ctypes.byref(a), count.data_ptr(), s), "pa_decode_validate")
+    return int(count.item())

@@ -39,6 +39,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
+#include <string>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -981,6 +983,34 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   }
 }
 
+// ---- input validation (debug) -------------------------------------------------
+//
+// The decode kernels clamp table entries into the pool instead of checking
+// them; these count what a correct caller never passes: contexts above the
+// bound, and table entries j < ceil(ctx / B) outside [0, num_blocks).
+
+__global__ __launch_bounds__(kWave) void clear_count_kernel(int32_t* count) {
+  if (threadIdx.x == 0) *count = 0;
+}
+
+// One wave per sequence; lanes walk the table row.
+__global__ __launch_bounds__(kWave) void validate_kernel(const int32_t* tables, const int32_t* ctx_lens,
+                                                         int max_blocks, int block_size, int num_blocks,
+                                                         int max_ctx, int32_t* count) {
+  const int s = blockIdx.x;
+  const int ctx = ctx_lens[s];
+  int bad = 0;
+  if (threadIdx.x == 0 && ctx > max_ctx) bad = 1;
+  const int nb = ctx > 0 ? min((min(ctx, max_ctx) + block_size - 1) / block_size, max_blocks) : 0;
+  for (int j = threadIdx.x; j < nb; j += kWave) {
+    const int id = tables[int64_t(s) * max_blocks + j];
+    bad += (id < 0 || id >= num_blocks) ? 1 : 0;
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) bad += __shfl_xor(bad, m);
+  if (threadIdx.x == 0 && bad) atomicAdd(count, bad);
+}
+
 // ---- host side ---------------------------------------------------------------
 
 int log2_exact(int x) {
@@ -1210,10 +1240,62 @@ pa_status check_workspace(const Plan& plan, const void* ws, size_t bytes) {
   return ok();
 }
 
+// Scratch for the debug check inside pa_decode: one counter per device,
+// addressed through hipGetSymbolAddress (the host-side name is not a device
+// address).
+__device__ int32_t g_debug_count;
+
+bool debug_checks() {
+  static const bool on = [] {
+    const char* v = std::getenv("PAGEDKV_DEBUG");
+    return v && *v && std::string(v) != "0";
+  }();
+  return on;
+}
+
+pa_status launch_validate(const pa_decode_args* a, int max_ctx, int32_t* count, hipStream_t st) {
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(kWave), 0, st, count);
+  pa_status ps = launch_status("validation clear kernel");
+  if (ps != PA_OK) return ps;
+  hipLaunchKernelGGL(validate_kernel, dim3(unsigned(a->num_seqs)), dim3(kWave), 0, st, a->block_tables, a->ctx_lens,
+                     a->max_blocks, a->block_size, a->num_blocks, max_ctx, count);
+  return launch_status("validation kernel");
+}
+
+// With PAGEDKV_DEBUG set, pa_decode validates its device inputs first: the
+// stream is synchronised and the call fails with PA_E_INVAL, launching
+// nothing else, if any context or table entry is out of range.
+pa_status debug_validate(const pa_decode_args* a, int max_ctx, hipStream_t st) {
+  int32_t* count = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&count), HIP_SYMBOL(g_debug_count)) != hipSuccess)
+    return fail(PA_E_HIP, "hipGetSymbolAddress(debug counter) failed");
+  pa_status ps = launch_validate(a, max_ctx, count, st);
+  if (ps != PA_OK) return ps;
+  int32_t bad = 0;
+  if (hipMemcpyAsync(&bad, count, sizeof(bad), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(PA_E_HIP, "reading the validation count failed");
+  if (bad) return fail(PA_E_INVAL, "PAGEDKV_DEBUG: " + std::to_string(bad) + " out-of-range context or table entries");
+  return ok();
+}
+
 }  // namespace
 }  // namespace pkv
 
 using namespace pkv;
+
+extern "C" pa_status pa_decode_validate(const pa_decode_args* a, int32_t* count, pa_stream stream) {
+  Plan plan;
+  pa_status st = check_paged(a, &plan);
+  if (st != PA_OK) return st;
+  if (!count) return fail(PA_E_INVAL, "count is null");
+  if (a->num_seqs == 0) {
+    hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(kWave), 0, static_cast<hipStream_t>(stream), count);
+    return launch_status("validation clear kernel");
+  }
+  if (!a->block_tables || !a->ctx_lens) return fail(PA_E_INVAL, "null device pointer");
+  return launch_validate(a, plan.max_ctx, count, static_cast<hipStream_t>(stream));
+}
 
 extern "C" pa_status pa_decode_workspace_bytes(const pa_decode_args* a, size_t* bytes_out) {
   if (!bytes_out) return fail(PA_E_INVAL, "bytes_out is null");
@@ -1231,6 +1313,10 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   if (a->num_seqs == 0) return ok();
   if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->ctx_lens)
     return fail(PA_E_INVAL, "null device pointer");
+  if (debug_checks()) {
+    st = debug_validate(a, plan.max_ctx, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   st = check_workspace(plan, a->workspace, a->workspace_bytes);
   if (st != PA_OK) return st;
   const int eb = dtype_bytes(a->kv_dtype);
