@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-_STREAMS = ("lengths", "free_order", "q", "k", "v")
+_STREAMS = ("lengths", "free_order", "q", "k", "v", "q_rows")
 
 _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _BITS = {"f32": (torch.int32, np.uint32), "f16": (torch.int16, np.uint16),
@@ -247,6 +247,47 @@ def llama13b_beam(seed=0, parents=8, beams=4):
                      num_blocks=16384, max_blocks=4096 // 16, seed=seed)
 
 
+def prefill_chunks(name, prefix_lens, chunk_lens, shape, num_blocks, max_blocks, seed=0, info=None):
+    """Chunked prefill: sequence s holds prefix_lens[s] cached tokens, then the
+    step appends its chunk of chunk_lens[s] new tokens (their K/V written like
+    any growth) and the chunk's query rows attend over the whole cache.
+
+    The chunk rows' queries come from their own stream: ``info["q_rows"]`` is
+    ``[T][Hq][d]`` raw bits, T = sum(chunk_lens), rows grouped by sequence;
+    ``info["q_start"]`` holds the S + 1 row offsets.
+    """
+    Hq, Hkv, d, B, dtype = shape
+    log = _Log()
+    for s, p in enumerate(prefix_lens):
+        if p > 0:
+            log.setup.append(("alloc", s, int(p), log.take(int(p))))
+    for s, (p, n) in enumerate(zip(prefix_lens, chunk_lens)):
+        if p > 0:
+            log.step.append(("append", s, int(n), log.take(int(n))))
+        else:
+            log.step.append(("alloc", s, int(n), log.take(int(n))))
+    rs = _streams(seed)
+    q_start = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    q_rows = normal_bits(rs["q_rows"], (int(q_start[-1]), Hq, d), dtype)
+    ctx = [int(p) + int(n) for p, n in zip(prefix_lens, chunk_lens)]
+    return _finish(name, log, range(len(chunk_lens)), shape, rs, num_blocks, max_blocks,
+                   dict(info or {}, ctx=ctx, prefix=list(map(int, prefix_lens)),
+                        chunk=list(map(int, chunk_lens)), q_rows=q_rows, q_start=q_start))
+
+
+PREFILL_CHUNK = 512
+
+
+def llama31_8b_prefill(seed=0, batch=16):
+    """Llama-3.1-8B-like layer (32/8 heads, d=128, bf16, B=16): 16 sequences
+    with cached prefixes of U{0..2048} tokens, each appending a 512-token chunk."""
+    prefix = _streams(seed)["lengths"].integers(0, 2048, size=batch, endpoint=True)
+    per_seq = (2048 + PREFILL_CHUNK) // 16
+    return prefill_chunks("llama31_8b_prefill_bf16", prefix.tolist(), [PREFILL_CHUNK] * batch,
+                          (32, 8, 128, 16, "bf16"), num_blocks=2 * batch * per_seq, max_blocks=per_seq,
+                          seed=seed)
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama7b": llama7b_mha,
@@ -257,4 +298,10 @@ CONFIGS = {
     "sweep32": lambda seed=0: block_sweep(32, seed),
     "long13b": llama13b_long,
     "beam13b": llama13b_beam,
+}
+
+PREFILL_CONFIGS = {
+    "prefill_small": lambda seed=0: prefill_chunks("prefill_small", [0, 17, 100, 300, 5], [1, 33, 64, 200, 16],
+                                                   (8, 2, 128, 16, "bf16"), 160, 32, seed=seed),
+    "prefill_gqa": llama31_8b_prefill,
 }
