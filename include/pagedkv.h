@@ -267,6 +267,45 @@ pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_ou
 pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
 
 /*
+ * Chunked prefill attention.  Sequence s holds ctx_lens[s] cached tokens, the
+ * last n_s = q_start[s+1] - q_start[s] of which are the chunk being
+ * prefilled: their K/V rows have been written (pa_write_kv) before the call.
+ * Chunk row i of s sits at position ctx_lens[s] - n_s + i and attends
+ * causally over tokens 0..position, gathered through the block table:
+ *     out[row][h] = sum_{t <= pos} softmax_t(scale * q[row][h] . K_t) * V_t
+ * ("vLLM PagedAttention：大模型推理的显存管理革命", 分配策略: prefill admits a
+ * prompt at once; "vllm-pagedattention", 它和 FlashAttention 优化的是两张不同的账:
+ * prefill works on large query blocks; "Paged Attention" (daiw.org), 回顾与衔接:
+ * a tiled kernel must read K/V through the block table).  Scores and p.V run
+ * on the matrix cores with float32 accumulation; the probabilities enter p.V
+ * as a 16-bit value plus the 16-bit rounding of its remainder.
+ */
+typedef struct pa_prefill_args {
+  void* out;                   /* [T][Hq][head_dim], out_dtype */
+  pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
+  const void* q;               /* [T][Hq][head_dim], kv_dtype: the chunks' rows, grouped by sequence */
+  const void* k_cache;         /* [num_blocks][Hkv][B][head_dim] */
+  const void* v_cache;
+  pa_dtype kv_dtype;           /* PA_F16 or PA_BF16 */
+  const int32_t* block_tables; /* [S][max_blocks] device */
+  const int32_t* ctx_lens;     /* [S] device: cached tokens, chunk included; <= 0 gives zero rows */
+  const int32_t* q_start;      /* [S + 1] device: rows of s are q_start[s] .. q_start[s+1]-1,
+                                  non-decreasing, q_start[S] = T, and each chunk no longer
+                                  than its context */
+  int32_t num_seqs;            /* S >= 0 */
+  int32_t num_rows;            /* T >= 0 */
+  int32_t num_q_heads;         /* Hq, a multiple of Hkv with Hq / Hkv in {1, 2, 4, 8} */
+  int32_t num_kv_heads;
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t block_size;          /* 8, 16 or 32 */
+  int32_t max_blocks;          /* table row width > 0 */
+  int32_t num_blocks;          /* physical blocks in the caches */
+  int32_t max_chunk;           /* >= every n_s; sizes the grid */
+  float scale;
+} pa_prefill_args;
+pa_status pa_prefill(const pa_prefill_args* args, pa_stream stream);
+
+/*
  * Debug check of pa_decode's device inputs.  The decode kernels clamp table
  * entries into the pool rather than check them (a corrupt table gives a
  * meaningless row, never an out-of-bounds read); this counts what a correct

@@ -69,6 +69,14 @@ class pa_contig_args(ctypes.Structure):
                 ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz)]
 
 
+class pa_prefill_args(ctypes.Structure):
+    _fields_ = [("out", c_vp), ("out_dtype", c_i32), ("q", c_vp), ("k_cache", c_vp), ("v_cache", c_vp),
+                ("kv_dtype", c_i32), ("block_tables", c_vp), ("ctx_lens", c_vp), ("q_start", c_vp),
+                ("num_seqs", c_i32), ("num_rows", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
+                ("head_dim", c_i32), ("block_size", c_i32), ("max_blocks", c_i32), ("num_blocks", c_i32),
+                ("max_chunk", c_i32), ("scale", c_f32)]
+
+
 _SIGS = {
     "pa_strerror": (ctypes.c_char_p, [c_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -93,6 +101,7 @@ _SIGS = {
     "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
     "pa_decode_set_waves": (c_i32, [c_i32]),
     "pa_decode_validate": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp, c_vp]),
+    "pa_prefill": (c_i32, [ctypes.POINTER(pa_prefill_args), c_vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -379,3 +388,36 @@ def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, s
     s = stream if stream is not None else current_stream(q.device)
     check(_lib.pa_decode_validate(ctypes.byref(a), count.data_ptr(), s), "pa_decode_validate")
     return int(count.item())
+
+
+def prefill_args(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scale, max_chunk):
+    nb, hkv, B, d = _cache_dims(k_cache)
+    T, hq, dq = q.shape
+    a = pa_prefill_args()
+    a.out = out.data_ptr() if out is not None else None
+    a.out_dtype = DTYPE_OF[out.dtype] if out is not None else PA_F32
+    a.q = q.data_ptr()
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.kv_dtype = DTYPE_OF[k_cache.dtype]
+    a.block_tables, a.ctx_lens, a.q_start = block_tables.data_ptr(), ctx_lens.data_ptr(), q_start.data_ptr()
+    a.num_seqs, a.num_rows = ctx_lens.shape[0], T
+    a.num_q_heads, a.num_kv_heads, a.head_dim = hq, hkv, d
+    a.block_size, a.max_blocks, a.num_blocks = B, block_tables.shape[1], nb
+    a.max_chunk, a.scale = max_chunk, scale
+    return a
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scale, max_chunk, stream=None):
+    """Chunked causal prefill attention into ``out`` ([T][Hq][d]); ``q_start``
+    ([S+1] int32, device) groups the rows by sequence; ``max_chunk`` bounds
+    every chunk's length."""
+    for t in (block_tables, ctx_lens, q_start):
+        if t.dtype != torch.int32:
+            raise ValueError("block_tables, ctx_lens and q_start must be int32")
+    for t in (out, q, k_cache, v_cache, block_tables, ctx_lens, q_start):
+        _dev(t)
+    if q_start.shape[0] != ctx_lens.shape[0] + 1:
+        raise ValueError("q_start needs num_seqs + 1 entries")
+    a = prefill_args(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scale, max_chunk)
+    check(_lib.pa_prefill(ctypes.byref(a), stream if stream is not None else current_stream(q.device)),
+          "pa_prefill")

@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # Device code: gfx950 only; packed float32 ops stay off (ordinary float code
 # is compiled to unpacked VALU instructions).
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["status.cpp", "pool.cpp", "cache_ops.hip", "decode.hip"]
+SOURCES = ["status.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
 
 
 def hipcc():

@@ -116,19 +116,6 @@ __device__ __forceinline__ void widen(BF16, uint4 c, float* o) {
   }
 }
 
-// float32 -> 16-bit output, round to nearest even.
-__device__ __forceinline__ uint16_t narrow(F16, float x) {
-  _Float16 h = (_Float16)x;
-  return __builtin_bit_cast(uint16_t, h);
-}
-
-__device__ __forceinline__ uint16_t narrow(BF16, float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
 // Lane-exchange steps within the 8 lanes of a row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -24,6 +24,23 @@ inline int dtype_bytes(pa_dtype t) {
 
 inline bool valid_dtype(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
 
+// float32 -> 16-bit, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t narrow(F16, float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint16_t narrow(BF16, float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// 16-bit -> float32, exact.
+__device__ __forceinline__ float widen1(F16, uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
+__device__ __forceinline__ float widen1(BF16, uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
 inline pa_status launch_status(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));

@@ -184,3 +184,24 @@ def test_wave_override_round_trip():
     assert lib.pa_decode_set_waves(3) == 96  # and up to at least 8
     assert lib.pa_decode_set_waves(0) == 8
     assert lib.pa_decode_set_waves(prev) == 0
+
+
+def test_prefill_rejects_before_launch():
+    lib = P.raw()
+    a = L.pa_prefill_args()
+    for k, v in dict(out=1, out_dtype=L.PA_F32, q=1, k_cache=1, v_cache=1, kv_dtype=L.PA_F32, block_tables=1,
+                     ctx_lens=1, q_start=1, num_seqs=2, num_rows=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     block_size=16, max_blocks=8, num_blocks=16, max_chunk=4, scale=0.1).items():
+        setattr(a, k, v)
+    assert lib.pa_prefill(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED     # float32 cache
+    a.kv_dtype = L.PA_BF16
+    for field, bad, code in [("head_dim", 96, L.PA_E_UNSUPPORTED), ("num_q_heads", 6, L.PA_E_UNSUPPORTED),
+                             ("block_size", 64, L.PA_E_UNSUPPORTED), ("scale", float("inf"), L.PA_E_INVAL),
+                             ("max_chunk", -1, L.PA_E_INVAL), ("num_rows", -1, L.PA_E_INVAL),
+                             ("out_dtype", L.PA_F16, L.PA_E_UNSUPPORTED)]:
+        good = getattr(a, field)
+        setattr(a, field, bad)
+        assert lib.pa_prefill(ctypes.byref(a), None) == code, field
+        setattr(a, field, good)
+    a.num_seqs = 0
+    assert lib.pa_prefill(ctypes.byref(a), None) == 0                      # nothing to do
