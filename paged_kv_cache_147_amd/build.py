@@ -24,6 +24,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # is compiled to unpacked VALU instructions).
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["status.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+# Per-source extras.  prefill: matrix-core accumulators in ordinary VGPRs, so
+# the softmax can rescale them in place (in AGPRs every step would copy them
+# out and back).
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():
@@ -38,7 +42,7 @@ def _compile(src):
     obj = os.path.join(OBJDIR, src + ".o")
     cmd = [hipcc(), *COMMON]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *HIP_FLAGS]
+        cmd += ["-x", "hip", *HIP_FLAGS, *EXTRA.get(src, [])]
     cmd += ["-c", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag; drop that note

@@ -13,15 +13,25 @@
 //
 // Work decomposition (a dense contraction, so the matrix cores do it):
 //   * one workgroup of 4 waves per (KV head, sequence, block of chunk
-//     tokens); each wave owns 16 (token, query head) rows -- 16/G tokens
-//     times the G query heads of the KV head;
-//   * the workgroup walks the keys its rows can see in steps of 32, staging
-//     each step's K and V rows (gathered through the block table) in LDS,
-//     double-buffered so the next step's loads fly during this one's math;
+//     tokens); each wave owns 32 (token, query head) rows -- 32/G tokens
+//     times the G query heads of the KV head -- as two 16-row MFMA tiles
+//     that share every K and V operand read from LDS;
+//   * the workgroup walks the keys its rows can see in steps of 32.  Each
+//     step's K and V rows are gathered through the block table straight into
+//     LDS by global_load_lds_dwordx4 (16 bytes per lane, no registers on the
+//     way), into a ring of 4 stages, so three steps of loads are in flight
+//     while one is computed; the block ids come from scalar loads, which keeps
+//     the vector-memory counter for the ring alone;
+//   * rows sit in LDS unpadded, their 16-byte chunks permuted by an XOR of
+//     the row index, so the K reads and the transposing V reads below spread
+//     over the banks;
 //   * scores are S^T = K Q^T (v_mfma_f32_16x16x32, A = 16 K rows from LDS,
 //     B = the wave's queries, held in registers), so each lane ends up with
-//     4 keys x 2 tiles of one row: the online softmax (running max, sum and
-//     rescale) is lane-local plus two cross-lane steps;
+//     4 keys x 2 tiles of one row and the softmax is lane-local: the running
+//     max moves only when a score exceeds it by more than 2^8 (until then the
+//     probabilities are exponentials against the stale max, at most 2^8, and
+//     the final division by the sum, taken against the same max, cancels
+//     it), the sum is kept per lane and added across lanes once at the end;
 //   * the same 8 probabilities per lane are, unchanged, the B operand of
 //     O^T += V^T P^T -- with the contraction's 32 keys ordered so that lane
 //     group q holds keys 4q..4q+3 and 16+4q..16+4q+3 -- and V^T comes from
@@ -30,7 +40,9 @@
 //     one column of 4);
 //   * P is split into a 16-bit high part and the 16-bit rounding of the
 //     remainder, two MFMAs per block, so p.V keeps ~16 more bits than a
-//     16-bit P would (a single rounded P alone exceeds the 1e-3 tolerance).
+//     16-bit P would (a single rounded P alone exceeds the 1e-3 tolerance);
+//   * workgroups are issued longest first (the last chunk blocks see the
+//     most keys), so the short ones fill the tail.
 #include "device_common.h"
 
 #include <cmath>
@@ -42,28 +54,104 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;                  // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kKeys = 32;                  // keys per step: two 16-key MFMA tiles
-constexpr int kRows = 16;                  // (token, query head) rows per wave
+constexpr int kSub = 2;                    // 16-row MFMA tiles per wave
+constexpr int kRows = 16 * kSub;           // (token, query head) rows per wave
+constexpr int kStages = 4;                 // LDS ring depth, in steps
+constexpr float kSlack = 8.f;              // log2 headroom before the running max moves
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // staged chunk: a plain vector, kept in registers
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) int32_t* const_i32_p;   // read through the scalar cache
 
-__device__ __forceinline__ f32x4_t mfma(BF16, uint4 a, uint4 b, f32x4_t c) {
+__device__ __forceinline__ f32x4_t mfma(BF16, u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                   c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma(F16, uint4 a, uint4 b, f32x4_t c) {
+__device__ __forceinline__ f32x4_t mfma(F16, u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-// LDS rows of staged K/V hold D elements plus 16 of padding: consecutive rows
-// then start 8 banks apart, so the 16 rows a transposing read touches spread
-// over the banks.
-template <int D>
-constexpr int lds_stride() { return D + 16; }
+// Two probabilities -> a packed 16-bit high part (round to nearest even) and
+// the packed 16-bit rounding of what the high part leaves out.
+__device__ __forceinline__ void split(BF16, float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){ra, rb}, bf16x2_t));
+}
+__device__ __forceinline__ void split(F16, float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f16x2_t h = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const f32x2_t hw = __builtin_convertvector(h, f32x2_t);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - hw.x, b - hw.y}, f16x2_t));
+}
+
+// Max / sum with the lane 16 or 32 positions away: after a permlane swap of
+// x with itself the two results hold x of the lane and of its partner.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Chunk permutation of a staged row: a row of CPR 16-byte chunks keeps chunk
+// c at position c ^ swizzle(row).  Rows 0..7 get 8 different values (the 8
+// rows one K read serves at a time use 8 different bank groups) and rows
+// 4k..4k+3 differ above bit 0 (the 4 rows of one transposing read, 32 bytes
+// each, land on different chunk pairs).  Adding 16 to the row leaves it alone.
+template <int CPR>
+__device__ __forceinline__ int swizzle(int row) {
+  return ((row & (CPR / 2 - 1)) << 1) | ((row / (CPR / 2)) & 1);
+}
+
+// Wait until this wave has at most N vector-memory operations outstanding
+// (the LDS ring's loads are the only ones in the loop), then meet the other
+// waves: after it, every wave's loads of the awaited step are in LDS and
+// every wave is done reading the stage the next loads overwrite.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_and_meet() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// One ring load: 16 bytes from base + off (base the same for the whole wave,
+// off per lane) into LDS at lds + 16 * lane (lds the same for the whole
+// wave), by global_load_lds_dwordx4 with a scalar base, whose LDS address is
+// M0 (saved and restored here; the s_nop covers the M0-write-to-LDS-DMA
+// hazard).  It is issued from asm so that the compiler, which cannot tell
+// which stage a load targets, adds no waits of its own for it in front of
+// the LDS reads: the ring's waits are wait_and_meet above.
+__device__ __forceinline__ void ring_load(const char* base, uint32_t off, const char* lds) {
+  const uint32_t l = (uint32_t)(size_t)((__attribute__((address_space(3))) const char*)lds);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(off), "s"(base), "s"(l) : "memory");
+}
+
+// float32 pair -> packed 16-bit pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack2(BF16, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
 
 struct PrefillParams {
   void* out;
@@ -81,30 +169,33 @@ struct PrefillParams {
   int32_t log2_block;
   int32_t max_blocks;
   int32_t num_blocks;
+  int32_t row_blocks;    // workgroups per (sequence, KV head)
   int32_t out_f32;
   float scale_log2e;     // scale * log2(e): scores in the log2 domain
 };
 
 template <class T, int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
-  constexpr int RS = lds_stride<D>();
   constexpr int KK = D / 32;              // score MFMA steps over head_dim
   constexpr int NN = D / 16;              // 16-column blocks of the output
+  constexpr int CPR = D / 8;              // 16-byte chunks per K or V row
+  constexpr int ROW = D * 2;              // bytes per staged row
+  constexpr int TILE = kKeys * ROW;       // bytes of one step's K (or V) rows
+  constexpr int NDMA = TILE / (kThreads * 16);   // 16-byte pieces per thread per tile
+  constexpr int NL = 2 * NDMA;            // ring loads per lane per step (K and V)
   constexpr int TPW = kRows / G;          // chunk tokens per wave
   constexpr int TPB = TPW * kWaves;       // chunk tokens per workgroup
-  constexpr int CPR = D / 8;              // 16-byte chunks per K or V row
-  constexpr int CPT = kKeys * CPR;        // chunks per 32-key tile
-  constexpr int NLD = 2 * CPT / kThreads; // K + V chunks each thread stages per step
-  static_assert(2 * CPT % kThreads == 0, "staging must divide evenly");
+  static_assert(TILE % (kThreads * 16) == 0, "a step's tile must split into whole wave loads");
+  static_assert((kStages - 2) * NL < 64, "vmcnt holds at most 63");
 
-  __shared__ __align__(16) uint16_t kbuf[2][kKeys * RS];
-  __shared__ __align__(16) uint16_t vbuf[2][kKeys * RS];
+  __shared__ __align__(16) char lds[kStages][2][TILE];   // [stage][K, V][32 rows]
 
   // Workgroup id -> (block of chunk tokens, sequence, KV head).  KV heads of
   // one sequence and then sequences vary fastest, so with S * Hkv a multiple
-  // of 8 every (sequence, KV head) keeps its workgroups on one XCD.
+  // of 8 every (sequence, KV head) keeps its workgroups on one XCD; the last
+  // chunk blocks, which see the most keys, go first.
   const int units = p.num_seqs * p.num_kv_heads;
-  const int rb = blockIdx.x / units;
+  const int rb = p.row_blocks - 1 - int(blockIdx.x) / units;
   const int unit = blockIdx.x % units;
   const int s = unit / p.num_kv_heads;
   const int g = unit % p.num_kv_heads;
@@ -120,15 +211,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const int m16 = lane & 15;              // MFMA column: this lane's (token, head) row
+  const int m16 = lane & 15;              // MFMA column: this lane's row within a tile
   const int q4 = lane >> 4;               // MFMA k-group
-  const int tok = tok0 + wave * TPW + m16 / G;
-  const bool row_ok = tok < n && r0 + tok >= 0 && r0 + tok < p.num_rows;
-  const int head = g * G + m16 % G;
+  const int tokw = tok0 + wave * TPW;     // first chunk token of this wave
+  const int head = g * G + m16 % G;       // the same in both tiles (16 is a multiple of G)
+
+  int tok[kSub];
+  bool row_ok[kSub];
+#pragma unroll
+  for (int j = 0; j < kSub; ++j) {
+    tok[j] = tokw + (16 * j + m16) / G;
+    row_ok[j] = tok[j] < n && r0 + tok[j] >= 0 && r0 + tok[j] < p.num_rows;
+  }
 
   if (ctx <= 0) {                         // no context: zero rows (whole workgroup)
-    if (row_ok) {
-      const int64_t orow = (int64_t(r0 + tok) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      if (!row_ok[j]) continue;
+      const int64_t orow = (int64_t(r0 + tok[j]) * p.num_q_heads + head) * D;
       for (int d = q4; d < D; d += 4) {
         if (p.out_f32) reinterpret_cast<float*>(p.out)[orow + d] = 0.f;
         else reinterpret_cast<uint16_t*>(p.out)[orow + d] = 0;
@@ -137,149 +237,217 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     return;
   }
   const int base = ctx - n;               // position of chunk row 0
-  const int pos = row_ok ? max(base + tok, 0) : 0;
-  const int last_tok = min(tok0 + TPB, n) - 1;
-  const int kmax = max(base + last_tok, 0);   // last key any row here sees (<= ctx - 1)
+  // Visible keys: row at chunk token t sees positions 0..base + t.  Padding
+  // rows (past the chunk) see the whole context; nothing of them is written.
+  int pos[kSub];
+#pragma unroll
+  for (int j = 0; j < kSub; ++j) pos[j] = tok[j] < n ? max(base + tok[j], 0) : ctx - 1;
+  const int wave_first = tokw < n ? max(base + tokw, 0) : ctx - 1;          // fewest keys in the wave
+  const int wave_last = tokw < n ? max(base + min(tokw + TPW, n) - 1, 0) : -1;  // most keys; -1: no rows
+  const int kmax = max(base + min(tok0 + TPB, n) - 1, 0);   // last key any row here sees (<= ctx - 1)
   const int nsteps = kmax / kKeys + 1;
 
-  // Queries: the B operand of S^T = K Q^T.  Lane (q4, m16) holds elements
-  // [32 kk + 8 q4, +8) of row m16 for step kk.
-  uint4 qb[KK];
-  {
-    const int qr = row_ok ? r0 + tok : 0;  // padding rows read row 0; never written
-    const char* qrow = reinterpret_cast<const char*>(p.q) + (int64_t(qr) * p.num_q_heads + head) * D * 2 + q4 * 16;
+  // Ring loads.  One wave-wide load moves 1 KB, RPI whole rows: load c of
+  // wave w fills tile rows [(c kWaves + w) RPI, +RPI), which lie in one cache
+  // block (RPI divides B), so its block id is one scalar load.  Lane l of it
+  // fills LDS slot 16 l of those rows: row lrow[c] of its block (within the
+  // tile), chunk position l % CPR, which holds chunk (l % CPR) ^ swizzle(row).
+  constexpr int RPI = kWave * 16 / ROW;   // rows per wave-wide load: 4 or 8
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int bmask = (1 << p.log2_block) - 1;
+  int lrow[NDMA];
+  uint32_t lbyte[NDMA];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qb[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 64);
+  for (int c = 0; c < NDMA; ++c) {
+    const int row = (c * kWaves + wv) * RPI + lane / CPR;
+    lrow[c] = row & bmask;
+    lbyte[c] = ((lane % CPR) ^ swizzle<CPR>(row)) * 16;
+  }
+  const const_i32_p table = (const_i32_p)(p.tables + int64_t(s) * p.max_blocks);
+  const int last_blk = (ctx - 1) >> p.log2_block;
+  const int last_row = (ctx - 1) & bmask;
+  const int64_t head_off = int64_t(g) * p.tile_bytes;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * p.tile_bytes;
+  auto issue = [&](int step) {
+    const int fb = (step * kKeys) >> p.log2_block;   // a step spans whole blocks: B divides 32
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) {
+      // keys past the context re-read rows of the last block (their scores are masked)
+      const int bidx = min(fb + (((c * kWaves + wv) * RPI) >> p.log2_block), last_blk);
+      const int blk = min(max(table[bidx], 0), p.num_blocks - 1);
+      const int cap = bidx == last_blk ? last_row : bmask;
+      const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
+      const int64_t at = int64_t(blk) * blk_stride + head_off;
+      const int dst = (c * kWaves + wv) * kWave * 16;
+      ring_load(p.k + at, off, lds[step % kStages][0] + dst);
+      ring_load(p.v + at, off, lds[step % kStages][1] + dst);
+    }
+  };
+
+  // Step 0's ring loads go first; the query loads follow, and one wait the
+  // compiler sees covers both, so that no wait for the queries is left for
+  // it to place inside the loop (where it would drain the ring).
+  issue(0);
+  // Queries: the B operand of S^T = K Q^T.  Lane (q4, m16) of tile j holds
+  // elements [32 kk + 8 q4, +8) of row 16 j + m16 for step kk.
+  u32x4_t qb[kSub][KK];
+#pragma unroll
+  for (int j = 0; j < kSub; ++j) {
+    const int qr = row_ok[j] ? r0 + tok[j] : 0;   // padding rows read row 0; never written
+    const char* qrow = reinterpret_cast<const char*>(p.q) + (int64_t(qr) * p.num_q_heads + head) * ROW + q4 * 16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb[j][kk] = *reinterpret_cast<const u32x4_t*>(qrow + kk * 64);
   }
 
-  // Staging: thread tid moves chunks tid + kThreads * c of the step's K tile
-  // (chunk index < CPT) and V tile, each chunk 16 bytes of one key row.
-  // Keys past the context re-read the last token (their scores are masked).
-  const int32_t* table = p.tables + int64_t(s) * p.max_blocks;
-  u32x4_t ld[NLD];
-  auto stage_load = [&](int t0) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0); expcnt and lgkmcnt left alone
+  // Scores are kept raw (q . k) and scaled inside the exponent, which needs
+  // a positive factor: a negative scale is moved into the queries by flipping
+  // their sign bits (exact), and a zero one is raised to 1e-30 (every
+  // exponent then still rounds to 0).
+  if (p.scale_log2e < 0.f) {
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
-      const int idx = tid + kThreads * c;
-      const bool is_v = idx >= CPT;
-      const int cc = is_v ? idx - CPT : idx;
-      const int key = min(t0 + cc / CPR, ctx - 1);
-      const int blk = min(max(table[key >> p.log2_block], 0), p.num_blocks - 1);
-      const char* src = (is_v ? p.v : p.k) + (int64_t(blk) * p.num_kv_heads + g) * p.tile_bytes +
-                        int64_t(key & ((1 << p.log2_block) - 1)) * D * 2 + (cc % CPR) * 16;
-      ld[c] = *reinterpret_cast<const u32x4_t*>(src);
-    }
-  };
-  auto stage_store = [&](int b) {
+    for (int j = 0; j < kSub; ++j)
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
-      const int idx = tid + kThreads * c;
-      const bool is_v = idx >= CPT;
-      const int cc = is_v ? idx - CPT : idx;
-      uint16_t* dst = (is_v ? vbuf[b] : kbuf[b]) + (cc / CPR) * RS + (cc % CPR) * 8;
-      *reinterpret_cast<u32x4_t*>(dst) = ld[c];
-    }
-  };
+      for (int kk = 0; kk < KK; ++kk) qb[j][kk] ^= 0x80008000u;
+  }
+#pragma unroll
+  for (int st = 1; st < kStages - 1; ++st)
+    if (st < nsteps) issue(st);
 
-  float run_m = -INFINITY, run_l = 0.f;   // this lane's row (m16)
-  f32x4_t o[NN];                          // O^T: lane holds columns 16 nn + 4 q4 + i of row m16
+  // LDS read offsets.  K (A operand of S^T): lane (q4, m16) reads key row
+  // m16 (+16 for the second tile), chunk 4 kk + q4.  V^T (transposing reads):
+  // lane m16 of group q4 points at row 4 q4 + m16 / 4 (+16 for keys 16..31),
+  // columns 16 nn + 4 (m16 % 4) .. +3, i.e. chunk 2 nn + (m16 % 4) / 2, and
+  // receives column 16 nn + m16 of the 4 rows its group addressed.
+  int koff[KK], voff[NN];
 #pragma unroll
-  for (int nn = 0; nn < NN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = m16 * ROW + ((4 * kk + q4) ^ swizzle<CPR>(m16)) * 16;
+  {
+    const int vr = 4 * q4 + (m16 >> 2);
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn)
+      voff[nn] = vr * ROW + ((2 * nn + ((m16 & 3) >> 1)) ^ swizzle<CPR>(vr)) * 16 + 8 * (m16 & 1);
+  }
 
-  auto compute = [&](int b, int t0) {
-    // S^T tiles: element i of tile j is key t0 + 16 j + 4 q4 + i of row m16.
-    float sc[8];
-    float mx = -INFINITY;
+  const float c = fmaxf(fabsf(p.scale_log2e), 1e-30f);
+  const float slack = kSlack / c;         // kSlack in raw score units
+  float run_m[kSub], run_mc[kSub], run_l[kSub];   // running max (raw), times c, this lane's part of the sum
+  f32x4_t o[kSub][NN];                    // O^T: lane holds columns 16 nn + 4 q4 + i of row m16
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = kbuf[b] + (16 * j + m16) * RS + 8 * q4;
+  for (int j = 0; j < kSub; ++j) {
+    run_m[j] = run_mc[j] = -INFINITY;
+    run_l[j] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = mfma(T{}, *reinterpret_cast<const uint4*>(krow + 32 * kk), qb[kk], acc);
+    for (int nn = 0; nn < NN; ++nn) o[j][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int step, auto masked_step) {
+    constexpr bool masked = decltype(masked_step)::value;   // some row of the wave stops inside this step
+    const int t0 = step * kKeys;
+    const char* kt = lds[step % kStages][0];
+    const char* vt = lds[step % kStages][1];
+    // S^T tiles: element i of acc[j][h] is key t0 + 16 h + 4 q4 + i of row 16 j + m16.
+    f32x4_t acc[kSub][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * j + 4 * q4 + i;
-        const float x = t > pos ? -INFINITY : acc[i] * p.scale_log2e;   // causal mask (and t >= ctx)
-        sc[4 * j + i] = x;
-        mx = fmaxf(mx, x);
+    for (int j = 0; j < kSub; ++j) acc[j][0] = acc[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kt + koff[kk]);
+      const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kt + koff[kk] + 16 * ROW);
+#pragma unroll
+      for (int j = 0; j < kSub; ++j) {
+        acc[j][0] = mfma(T{}, k0, qb[j][kk], acc[j][0]);
+        acc[j][1] = mfma(T{}, k1, qb[j][kk], acc[j][1]);
       }
     }
-    // The row's 32 scores sit in lanes m16, m16 + 16, m16 + 32, m16 + 48.
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(run_m, mx);        // finite: key 0 is in every row's first step
-    const float f = __builtin_amdgcn_exp2f(run_m - mnew);
-    float pr[8], psum = 0.f;
+    u32x4_t PH[kSub], PL[kSub];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pr[e] = __builtin_amdgcn_exp2f(sc[e] - mnew);
-      psum += pr[e];
+    for (int j = 0; j < kSub; ++j) {
+      float x[8], mx = -INFINITY;
+      const int lim = pos[j] - t0 - 4 * q4;   // element e is visible when 16 (e / 4) + e % 4 <= lim
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = acc[j][e >> 2][e & 3];
+        if (masked && 16 * (e >> 2) + (e & 3) > lim) x[e] = -INFINITY;
+        mx = fmaxf(mx, x[e]);
+      }
+      // The max moves only when some score of the wave's rows exceeds it by
+      // more than kSlack in log2 units (always in the first step, where it
+      // is -inf).
+      if (__builtin_amdgcn_ballot_w64(mx > run_m[j] + slack)) {
+        const float mnew = fmaxf(run_m[j], max_xor32(max_xor16(mx)));
+        const float f = __builtin_amdgcn_exp2f((run_m[j] - mnew) * c);
+        run_m[j] = mnew;
+        run_mc[j] = mnew * c;
+        run_l[j] *= f;
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) o[j][nn] *= f;
+      }
+      float pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -run_mc[j]));
+        run_l[j] += pr[e];
+      }
+      // P^T operand: contraction index 8 q4 + e is key 4 q4 + e (e < 4) or
+      // 16 + 4 q4 + e - 4 (e >= 4), i.e. exactly pr[e].
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hi, lo;
+        split(T{}, pr[2 * e], pr[2 * e + 1], hi, lo);
+        PH[j][e] = hi;
+        PL[j][e] = lo;
+      }
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    run_l = run_l * f + psum;
-    run_m = mnew;
-#pragma unroll
-    for (int nn = 0; nn < NN; ++nn) o[nn] *= f;
-
-    // P^T operands: contraction index 8 q4 + e is key 4 q4 + e (e < 4) or
-    // 16 + 4 q4 + e - 4 (e >= 4), i.e. exactly pr[e]; high and low parts.
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t h0 = narrow(T{}, pr[2 * e]), h1 = narrow(T{}, pr[2 * e + 1]);
-      const uint16_t l0 = narrow(T{}, pr[2 * e] - widen1(T{}, h0));
-      const uint16_t l1 = narrow(T{}, pr[2 * e + 1] - widen1(T{}, h1));
-      ph[e] = uint32_t(h0) | (uint32_t(h1) << 16);
-      pl[e] = uint32_t(l0) | (uint32_t(l1) << 16);
-    }
-    const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-    const uint4 PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-
-    // V^T operands by transposing reads: lane m16 of group q4 points at row
-    // 4 q4 + m16 / 4 (then 16 + that), columns 16 nn + 4 (m16 % 4) .. +3, and
-    // receives column 16 nn + m16 of the 4 rows its group addressed.
-    const uint16_t* vlo = vbuf[b] + (4 * q4 + (m16 >> 2)) * RS + 4 * (m16 & 3);
-    const uint16_t* vhi = vlo + 16 * RS;
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) {
       const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(vlo + 16 * nn));
+          (__attribute__((address_space(3))) i16x4_t*)(vt + voff[nn]));
       const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(vhi + 16 * nn));
+          (__attribute__((address_space(3))) i16x4_t*)(vt + voff[nn] + 16 * ROW));
       const uint2 w0 = __builtin_bit_cast(uint2, a0), w1 = __builtin_bit_cast(uint2, a1);
-      const uint4 A = make_uint4(w0.x, w0.y, w1.x, w1.y);
-      o[nn] = mfma(T{}, A, PH, o[nn]);
-      o[nn] = mfma(T{}, A, PL, o[nn]);
+      const u32x4_t va = {w0.x, w0.y, w1.x, w1.y};
+#pragma unroll
+      for (int j = 0; j < kSub; ++j) {
+        o[j][nn] = mfma(T{}, va, PH[j], o[j][nn]);
+        o[j][nn] = mfma(T{}, va, PL[j], o[j][nn]);
+      }
     }
   };
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
+  // Ring: step st lives in stage st % kStages.  Before computing step st the
+  // wave waits for its own loads of st (the later steps' loads, at most
+  // kStages - 2 of them, stay in flight) and meets the others; the stage it
+  // then refills held step st - 1, which every wave has finished.
   for (int st = 0; st < nsteps; ++st) {
-    const int b = st & 1;
-    // The next step's rows fly during this step's math (after the last step
-    // this re-reads clamped rows into the idle buffer; nothing uses them).
-    stage_load((st + 1) * kKeys);
-    compute(b, st * kKeys);
-    stage_store(b ^ 1);   // buffer b ^ 1 was last read before the previous barrier
-    __syncthreads();
+    const int ahead = min(kStages - 2, nsteps - 1 - st);   // later steps already issued
+    if (ahead >= 2) wait_and_meet<2 * NL>();
+    else if (ahead == 1) wait_and_meet<NL>();
+    else wait_and_meet<0>();
+    if (st + kStages - 1 < nsteps) issue(st + kStages - 1);
+    if (st * kKeys <= wave_last) {                      // some row of the wave sees this step
+      if (st * kKeys + kKeys - 1 > wave_first) compute(st, std::true_type{});
+      else compute(st, std::false_type{});
+    }
   }
 
-  if (!row_ok) return;
-  const float inv = 1.f / run_l;
-  const int64_t orow = (int64_t(r0 + tok) * p.num_q_heads + head) * D;
+  // the loop's last wait drained the ring; rows of the wave now end
 #pragma unroll
-  for (int nn = 0; nn < NN; ++nn) {
-    const int d0 = 16 * nn + 4 * q4;
-    const float x0 = o[nn][0] * inv, x1 = o[nn][1] * inv, x2 = o[nn][2] * inv, x3 = o[nn][3] * inv;
-    if (p.out_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow + d0) = make_float4(x0, x1, x2, x3);
-    } else {
-      const uint32_t w0 = uint32_t(narrow(T{}, x0)) | (uint32_t(narrow(T{}, x1)) << 16);
-      const uint32_t w1 = uint32_t(narrow(T{}, x2)) | (uint32_t(narrow(T{}, x3)) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow + d0) = make_uint2(w0, w1);
+  for (int j = 0; j < kSub; ++j) {
+    const float l = sum_xor32(sum_xor16(run_l[j]));     // the row's 4 lanes' parts
+    if (!row_ok[j]) continue;
+    const float inv = 1.f / l;
+    const int64_t orow = (int64_t(r0 + tok[j]) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const int d0 = 16 * nn + 4 * q4;
+      const float x0 = o[j][nn][0] * inv, x1 = o[j][nn][1] * inv, x2 = o[j][nn][2] * inv, x3 = o[j][nn][3] * inv;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow + d0) = make_float4(x0, x1, x2, x3);
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow + d0) =
+            make_uint2(pack2(T{}, x0, x1), pack2(T{}, x2, x3));
+      }
     }
   }
 }
@@ -358,6 +526,7 @@ extern "C" pa_status pa_prefill(const pa_prefill_args* a, pa_stream stream) {
   pp.out_f32 = a->out_dtype == PA_F32;
   pp.scale_log2e = a->scale * 1.4426950408889634f;
   const int64_t rbs = (int64_t(a->max_chunk) + tokens_per_workgroup(G) - 1) / tokens_per_workgroup(G);
+  pp.row_blocks = int(rbs);
   const dim3 grid(unsigned(rbs * a->num_seqs * a->num_kv_heads));
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (a->kv_dtype == PA_BF16) {
