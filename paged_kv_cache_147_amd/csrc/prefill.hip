@@ -57,6 +57,8 @@ constexpr int kKeys = 32;                  // keys per step: two 16-key MFMA til
 constexpr int kSub = 2;                    // 16-row MFMA tiles per wave
 constexpr int kRows = 16 * kSub;           // (token, query head) rows per wave
 constexpr int kStages = 4;                 // LDS ring depth, in steps
+constexpr int kXcds = 8;                   // workgroups are dealt to the XCDs round robin
+constexpr int kRankMax = 256;              // units per XCD ranked by context length (else taken in order)
 constexpr float kSlack = 8.f;              // log2 headroom before the running max moves
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -134,15 +136,26 @@ __device__ __forceinline__ void wait_and_meet() {
 // One ring load: 16 bytes from base + off (base the same for the whole wave,
 // off per lane) into LDS at lds + 16 * lane (lds the same for the whole
 // wave), by global_load_lds_dwordx4 with a scalar base, whose LDS address is
-// M0 (saved and restored here; the s_nop covers the M0-write-to-LDS-DMA
-// hazard).  It is issued from asm so that the compiler, which cannot tell
+// M0 (saved and restored here).  It is issued from asm so that the compiler, which cannot tell
 // which stage a load targets, adds no waits of its own for it in front of
 // the LDS reads: the ring's waits are wait_and_meet above.
 __device__ __forceinline__ void ring_load(const char* base, uint32_t off, const char* lds) {
-  const uint32_t l = (uint32_t)(size_t)((__attribute__((address_space(3))) const char*)lds);
+  // Both are the same in every lane; readfirstlane puts them in scalar
+  // registers.  It returns a signed int: each half is taken back through
+  // uint32_t, so the low half of the address is zero-extended, never
+  // sign-extended into the high half.
+  const uint32_t l = uint32_t(
+      __builtin_amdgcn_readfirstlane(int(uint32_t(size_t((__attribute__((address_space(3))) const char*)lds)))));
+  const uint64_t b = uint64_t(uintptr_t(base));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32))));
+  const uint64_t sb = (uint64_t(hi) << 32) | uint64_t(lo);
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(off), "s"(base), "s"(l) : "memory");
+  // s_nop 4 gives the 5 wait states a vector-ALU write of the base's scalar
+  // registers (readfirstlane) needs before a memory instruction reads them;
+  // the compiler's hazard checks do not look inside this asm.
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(off), "s"(sb), "s"(l) : "memory");
 }
 
 // float32 pair -> packed 16-bit pair, round to nearest even.
@@ -169,7 +182,7 @@ struct PrefillParams {
   int32_t log2_block;
   int32_t max_blocks;
   int32_t num_blocks;
-  int32_t row_blocks;    // workgroups per (sequence, KV head)
+  int32_t row_blocks;    // chunk blocks per (sequence, KV head)
   int32_t out_f32;
   float scale_log2e;     // scale * log2(e): scores in the log2 domain
 };
@@ -190,13 +203,44 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 
   __shared__ __align__(16) char lds[kStages][2][TILE];   // [stage][K, V][32 rows]
 
-  // Workgroup id -> (block of chunk tokens, sequence, KV head).  KV heads of
-  // one sequence and then sequences vary fastest, so with S * Hkv a multiple
-  // of 8 every (sequence, KV head) keeps its workgroups on one XCD; the last
-  // chunk blocks, which see the most keys, go first.
+  const int tid = threadIdx.x;
+
+  // Workgroup id -> (unit = (sequence, KV head), block of chunk tokens).
+  // Workgroup ids go to the XCDs round robin; XCD x takes the units
+  // u = x + 8 m.  It runs them one after another in order of decreasing
+  // context, and all chunk blocks of a unit in a row, the last (which see
+  // the most keys) first, so that a unit's K and V rows are fetched into
+  // that XCD's L2 once while its blocks run side by side, and the longest
+  // units do not start last.
   const int units = p.num_seqs * p.num_kv_heads;
-  const int rb = p.row_blocks - 1 - int(blockIdx.x) / units;
-  const int unit = blockIdx.x % units;
+  const int xcd = blockIdx.x % kXcds;
+  const int local = blockIdx.x / kXcds;
+  const int nx = (units - xcd + kXcds - 1) / kXcds;       // units of this XCD
+  const int rank = local / p.row_blocks;
+  const int rb = p.row_blocks - 1 - local % p.row_blocks;
+  if (rank >= nx) return;                 // grid padding (the whole workgroup)
+  int m = rank;                           // unit xcd + 8 m has this rank
+  if (nx > 1 && nx <= kRankMax) {
+    // rank of each unit: how many of the XCD's units have a longer context
+    // (ties: the lower index first); scratch in the last ring stage, which
+    // the first loads below leave alone
+    int* len = reinterpret_cast<int*>(lds[kStages - 1][1]);
+    int* pick = len + kRankMax;
+    if (tid < nx) len[tid] = p.ctx_lens[(xcd + kXcds * tid) / p.num_kv_heads];
+    __syncthreads();
+    if (tid < nx) {
+      const int mine = len[tid];
+      int r = 0;
+      for (int t = 0; t < nx; ++t) {
+        const int o = len[t];
+        r += o > mine || (o == mine && t < tid);
+      }
+      if (r == rank) *pick = tid;
+    }
+    __syncthreads();
+    m = *pick;
+  }
+  const int unit = xcd + kXcds * m;
   const int s = unit / p.num_kv_heads;
   const int g = unit % p.num_kv_heads;
   const int r0 = p.q_start[s];
@@ -208,7 +252,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // the tables, q or out (their results are then meaningless).
   const int ctx = min(p.ctx_lens[s], p.max_blocks << p.log2_block);
 
-  const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int m16 = lane & 15;              // MFMA column: this lane's row within a tile
@@ -268,13 +311,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int last_row = (ctx - 1) & bmask;
   const int64_t head_off = int64_t(g) * p.tile_bytes;
   const int64_t blk_stride = int64_t(p.num_kv_heads) * p.tile_bytes;
-  auto issue = [&](int step) {
-    const int fb = (step * kKeys) >> p.log2_block;   // a step spans whole blocks: B divides 32
+  // The block ids of a step are fetched (scalar loads) one step before its
+  // loads are issued, so their latency hides behind a step of math.
+  int ids[NDMA];
+  auto block_index = [&](int step, int c) {
+    // a step spans whole blocks (B divides 32); keys past the context
+    // re-read rows of the last block (their scores are masked)
+    return min(((step * kKeys) >> p.log2_block) + (((c * kWaves + wv) * RPI) >> p.log2_block), last_blk);
+  };
+  auto fetch = [&](int step) {
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) ids[c] = table[block_index(step, c)];
+  };
+  auto issue = [&](int step) {            // ids hold this step's block ids
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
-      // keys past the context re-read rows of the last block (their scores are masked)
-      const int bidx = min(fb + (((c * kWaves + wv) * RPI) >> p.log2_block), last_blk);
-      const int blk = min(max(table[bidx], 0), p.num_blocks - 1);
+      const int bidx = block_index(step, c);
+      const int blk = min(max(ids[c], 0), p.num_blocks - 1);
       const int cap = bidx == last_blk ? last_row : bmask;
       const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
       const int64_t at = int64_t(blk) * blk_stride + head_off;
@@ -287,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // Step 0's ring loads go first; the query loads follow, and one wait the
   // compiler sees covers both, so that no wait for the queries is left for
   // it to place inside the loop (where it would drain the ring).
+  fetch(0);
   issue(0);
   // Queries: the B operand of S^T = K Q^T.  Lane (q4, m16) of tile j holds
   // elements [32 kk + 8 q4, +8) of row 16 j + m16 for step kk.
@@ -312,7 +366,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   }
 #pragma unroll
   for (int st = 1; st < kStages - 1; ++st)
-    if (st < nsteps) issue(st);
+    if (st < nsteps) {
+      fetch(st);
+      issue(st);
+    }
+  if (kStages - 1 < nsteps) fetch(kStages - 1);
 
   // LDS read offsets.  K (A operand of S^T): lane (q4, m16) reads key row
   // m16 (+16 for the second tile), chunk 4 kk + q4.  V^T (transposing reads):
@@ -429,6 +487,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       if (st * kKeys + kKeys - 1 > wave_first) compute(st, std::true_type{});
       else compute(st, std::false_type{});
     }
+    if (st + kStages < nsteps) fetch(st + kStages);
   }
 
   // the loop's last wait drained the ring; rows of the wave now end
@@ -481,7 +540,8 @@ pa_status check_prefill(const pa_prefill_args* a) {
   if (a->max_chunk < 0) return fail(PA_E_INVAL, "max_chunk must be >= 0");
   if (!std::isfinite(a->scale)) return fail(PA_E_INVAL, "scale must be finite");
   const int64_t rbs = (int64_t(a->max_chunk) + tokens_per_workgroup(G) - 1) / tokens_per_workgroup(G);
-  if (rbs * a->num_seqs * a->num_kv_heads > INT32_MAX) return fail(PA_E_UNSUPPORTED, "grid too large");
+  const int64_t units = int64_t(a->num_seqs) * a->num_kv_heads;
+  if (rbs * kXcds * ((units + kXcds - 1) / kXcds) > INT32_MAX) return fail(PA_E_UNSUPPORTED, "grid too large");
   return ok();
 }
 
@@ -527,7 +587,8 @@ extern "C" pa_status pa_prefill(const pa_prefill_args* a, pa_stream stream) {
   pp.scale_log2e = a->scale * 1.4426950408889634f;
   const int64_t rbs = (int64_t(a->max_chunk) + tokens_per_workgroup(G) - 1) / tokens_per_workgroup(G);
   pp.row_blocks = int(rbs);
-  const dim3 grid(unsigned(rbs * a->num_seqs * a->num_kv_heads));
+  const int64_t units = int64_t(a->num_seqs) * a->num_kv_heads;
+  const dim3 grid(unsigned(rbs * kXcds * ((units + kXcds - 1) / kXcds)));
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (a->kv_dtype == PA_BF16) {
     if (a->head_dim == 64) launch_prefill<BF16, 64>(pp, G, grid, hs);
