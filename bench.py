@@ -14,7 +14,14 @@ Prints ONE JSON line (rank 0, N = 1): value = logical KV bytes read per step
 every pa_decode launch in the timed region; ``cpu_baseline`` times the float64
 oracle on a bounded sample of the same batch.
 
+The line also carries a ``prefill`` object: pa_prefill (chunked causal
+prefill over the paged cache) on the Llama-3.1-8B-like prefill batch (16
+sequences, 512-token chunks after cached prefixes of 0..2048 tokens), in
+algorithmic TFLOP/s against the dense bf16 matrix-core peak, with its own
+roofline and oracle baseline.  ``--mode prefill`` prints that object alone.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--mode decode|prefill] [--no-prefill]
 """
 import argparse
 import hashlib
@@ -29,6 +36,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak); sequences/sec"
 PEAK_HBM_GBPS = 8000.0
+PREFILL_METRIC = "paged prefill attention: algorithmic TFLOP/s (% of MI355X dense bf16 matrix-core peak)"
+PEAK_MFMA_BF16_TFLOPS = 2500.0
 WORKLOADS = {
     "llama31_8b_gqa": ("gqa", "Llama-3.1-8B-like GQA decode layer, shared 1008-token prefixes"),
     "llama31_8b_gqa_noshare": ("gqa_noshare", "same lengths and bytes, every prefix private"),
@@ -40,6 +49,7 @@ WORKLOADS = {
     "llama13b_beam": ("beam13b", "8 parents x 4 beams at ctx 4096, copy-on-write"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_traffic.md")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_prefill_traffic.md")
 
 
 def log(*a):
@@ -60,12 +70,25 @@ def decode_bytes(wl, ctx):
     return kv, kv + other
 
 
-def source_digest():
+def source_digest(names=("decode.hip", "device_common.h")):
     h = hashlib.sha256()
-    for name in ("decode.hip", "device_common.h"):
+    for name in names:
         with open(os.path.join(ROOT, "paged_kv_cache_147_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_prefill_traffic():
+    """Per-launch HBM bytes of pa_prefill from the committed counter summary,
+    or None when the prefill source changed since the counters were taken."""
+    try:
+        text = open(PREFILL_TRAFFIC_FILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    m = re.search(r"^\|\s*llama31_8b_prefill\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.e+]+)\s*\|", text, flags=re.M)
+    if not m or m.group(1) != source_digest(("prefill.hip", "device_common.h")):
+        return None
+    return float(m.group(2))
 
 
 def measured_traffic(workload):
@@ -108,6 +131,129 @@ def cpu_baseline(wl, budget_s=10.0):
             "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB logical KV), "
                       f"{wall:.1f} s wall, float64 numpy",
             "seqs_per_s": round(done / wall, 2)}
+
+
+def prefill_flops(ctx, q_start, head_dim, num_q_heads):
+    """Algorithmic flops of one pa_prefill launch: a chunk row at position p
+    takes p + 1 dot products of length d (scores) and p + 1 d-wide
+    multiply-adds (p.V), 2 flops per multiply-add, for every query head.
+    Rows of a chunk of n sit at positions ctx - n .. ctx - 1."""
+    total = 0
+    for s in range(len(ctx)):
+        n = int(q_start[s + 1]) - int(q_start[s])
+        first = int(ctx[s]) - n
+        total += n * first + n * (n + 1) // 2
+    return total * 4 * head_dim * num_q_heads
+
+
+def prefill_cpu_baseline(wl, budget_s=10.0):
+    """The float64 prefill oracle, as it stands, on whole sequences of the
+    batch (all rows, all heads) until ~budget_s of work; in TFLOP/s."""
+    import numpy as np
+
+    from oracle import prefill as PF
+    from tests._replay import OracleRun
+    run = OracleRun(wl)
+    tables, lens = run.tables(wl)
+    qs = wl.info["q_start"]
+    done, flops, wall, cpu = 0, 0, 0.0, 0.0
+    while done < wl.num_seqs and wall < budget_s:
+        s = done
+        rows = [(r, h) for r in range(qs[s], qs[s + 1]) for h in range(wl.num_q_heads)]
+        t0, c0 = time.perf_counter(), time.process_time()
+        PF.paged_prefill(wl.info["q_rows"], run.cache.k, run.cache.v, tables, lens, qs, wl.block_size,
+                         wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads, rows=rows)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        flops += prefill_flops(lens[s:s + 1], [0, qs[s + 1] - qs[s]], wl.head_dim, wl.num_q_heads)
+        done += 1
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"first {done} of {wl.num_seqs} sequences, every chunk row and head "
+                      f"({flops / 1e9:.2f} GFLOP), {wall:.1f} s wall, float64 numpy"}
+
+
+def bench_prefill(steps, warmup, dev, with_cpu):
+    """pa_prefill on the Llama-3.1-8B-like prefill batch: each launch timed
+    with HIP events on the stream it runs on."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    import workloads as W
+    from tests._native import NativeDeviceRun, device_tensor
+    wl = W.llama31_8b_prefill()
+    run = NativeDeviceRun(wl, device=dev)
+    ctx = run.ctx_host.tolist()
+    qs = [int(x) for x in wl.info["q_start"]]
+    q = device_tensor(wl.info["q_rows"], wl.dtype, dev)
+    q_start = torch.tensor(qs, dtype=torch.int32, device=dev)
+    max_chunk = int(max(wl.info["chunk"]))
+    out = torch.empty((q.shape[0], wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    stream = P.current_stream(dev)
+    flops = prefill_flops(ctx, qs, wl.head_dim, wl.num_q_heads)
+
+    def call():
+        P.pa_prefill(out, q, run.k_cache, run.v_cache, run.tables, run.ctx, q_start, wl.scale, max_chunk,
+                     stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = [a.elapsed_time(b) for a, b in evs]
+    ms_call = elapsed * 1e3 / steps
+    avg = float(np.mean(ms))
+    log(f"[bench] prefill: {steps} launches, {ms_call:.4f} ms/call wall; kernel avg {avg:.4f} ms "
+        f"(p10 {np.percentile(ms, 10):.4f}, p90 {np.percentile(ms, 90):.4f})")
+    tflops = flops / (ms_call * 1e-3) / 1e12
+    achieved = flops / (avg * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_call, 5),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama31_8b_prefill",
+                   "description": "Llama-3.1-8B-like GQA layer, 16 sequences, 512-token chunks after "
+                                  "cached prefixes of 0..2048 tokens",
+                   "batch": wl.num_seqs, "chunk_rows": qs[-1], "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "kv_dtype": wl.dtype, "out_dtype": "f32", "ctx_mean": round(float(np.mean(ctx)), 1),
+                   "ctx_max": int(max(ctx)), "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "traffic": measured_prefill_traffic(), "kernel": "pa_prefill (one launch)",
+                     "avg_launch_ms": round(avg, 5), "flops_per_launch": flops,
+                     "launch_ms_p10_median_p90": [round(float(np.percentile(ms, x)), 5) for x in (10, 50, 90)]},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        log("[bench] timing the prefill oracle on a CPU sample ...")
+        res["cpu_baseline"] = prefill_cpu_baseline(wl)
+    return res
+
+
+def copy_calibration(dev):
+    """Three plain 1 GiB device copies: the reference for the HBM counters."""
+    import torch
+    a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
 
 def time_calls(fn, n, warm=5):
@@ -186,6 +332,10 @@ def main():
     ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("decode", "prefill"), default="decode",
+                    help="prefill: print only the pa_prefill measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="leave the prefill object out")
+    ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--compare-contiguous", action="store_true",
@@ -207,6 +357,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.mode == "prefill":
+        res = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        res.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
+        print(json.dumps(res), flush=True)
+        return
     key, desc = WORKLOADS[args.workload]
     t0 = time.time()
     wl = W.CONFIGS[key]()
@@ -262,12 +419,7 @@ def main():
         f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
 
     if args.copy_calibration:
-        a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+        copy_calibration(dev)
 
     comparison = None
     if args.compare_contiguous:
@@ -306,6 +458,8 @@ def main():
     }
     if comparison is not None:
         result["paged_vs_contiguous"] = comparison
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)
