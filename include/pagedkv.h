@@ -152,6 +152,64 @@ int32_t pa_pool_refcount(const pa_pool* pool, int32_t block);
 /* Free list front to back into out[0 .. min(cap, free)-1]; *n_out = free count. */
 pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
 
+/*
+ * Prefix cache (automatic prefix caching on top of the pool: a full block is
+ * identified by its parent block, its token ids and extra keys such as a
+ * cache salt, so a request whose prompt starts with a cached prefix reuses
+ * those blocks and skips their prefill -- "vllm-pagedattention"
+ * (chenyuan1125.github.io), the passage on automatic prefix caching after
+ * 一块内存，如何安全地属于多条序列; the salt keeps tenants' prefixes apart, same
+ * page, closing remarks).  Rules:
+ * - the key of a full block is (its parent block's id, salt, its B token
+ *   ids); lookups walk a prompt's full blocks from the first and stop at the
+ *   first miss, so a hit is always a whole-block prefix;
+ * - a block is registered when it becomes full -- at admission for the
+ *   prompt's full blocks, or when pa_seq_append_token fills it -- provided
+ *   its parent is registered (or it is a first block) and no block holds its
+ *   key yet;
+ * - a registered block whose reference count drops to 0 stays cached on the
+ *   free list; allocation still takes from the front, and a cached block
+ *   taken there is evicted (least recently released first); a hit takes a
+ *   free cached block back off the list;
+ * - with the cache on, pa_seq_free releases a sequence's blocks last to
+ *   first (descendants are evicted before their ancestors);
+ * - pa_seq_alloc, pa_seq_append and pa_seq_extend still work; they leave the
+ *   sequence's later blocks unregistered (their token ids are not known).
+ * The caller writes the K/V of the uncached tokens (slots from cached_tokens
+ * on) before any other request can hit the blocks it registered.
+ */
+typedef struct pa_prefix_stats_t {
+  int64_t lookups;       /* block keys looked up by pa_seq_alloc_prefix */
+  int64_t hit_blocks;    /* of them found and reused */
+  int64_t registered;    /* blocks registered */
+  int64_t evictions;     /* cached blocks taken off the free list for new contents */
+  int32_t cached_blocks; /* blocks registered now */
+} pa_prefix_stats_t;
+
+/* Switch the prefix cache on; only before the first sequence is admitted
+ * (PA_E_INVAL otherwise). */
+pa_status pa_pool_enable_prefix_cache(pa_pool* pool);
+
+/* Admit seq with its n_tokens >= 0 prompt token ids (host array) under salt.
+ * The longest cached whole-block prefix is reused; the rest takes fresh
+ * blocks.  *cached_tokens_out (nullable) = tokens whose K/V is already in
+ * the cache (a multiple of B, possibly n_tokens); slots_out (nullable)
+ * receives all n_tokens slots.  All-or-nothing: PA_E_NOBLOCKS when the free
+ * list (cached blocks included, the hits excepted) is short; PA_E_EXISTS,
+ * and PA_E_INVAL when the cache is off. */
+pa_status pa_seq_alloc_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens, int32_t n_tokens,
+                              uint64_t salt, int32_t* cached_tokens_out, int64_t* slots_out);
+
+/* pa_seq_append for a token whose id is known: as pa_seq_append, and when the
+ * token fills the last block, that block is registered (rules above). */
+pa_status pa_seq_append_token(pa_pool* pool, int64_t seq, int32_t token, int64_t* slot_out,
+                              int32_t* cow_src, int32_t* cow_dst);
+
+pa_status pa_prefix_cache_stats(const pa_pool* pool, pa_prefix_stats_t* out);
+/* 1 if the block is registered in the prefix cache, 0 if not, -1 for an id
+ * outside [0, num_blocks). */
+int32_t pa_pool_block_cached(const pa_pool* pool, int32_t block);
+
 /* ------------------------------------------------------------------------- */
 /* Device operations                                                          */
 /* ------------------------------------------------------------------------- */

@@ -65,6 +65,10 @@ class BlockPoolModel:
         self.length = {}   # seq id -> tokens held
 
     # -- helpers -----------------------------------------------------------
+    def _take(self):
+        """The block at the front of the free list."""
+        return self.free_list.popleft()
+
     def _slot(self, seq, pos):
         blk = self.tables[seq][pos // self.block_size]
         return blk * self.block_size + pos % self.block_size
@@ -83,7 +87,7 @@ class BlockPoolModel:
         want = -(-n_tokens // self.block_size)
         if want > len(self.free_list):
             raise PoolError("NOBLOCKS", f"need {want}, have {len(self.free_list)}")
-        table = [self.free_list.popleft() for _ in range(want)]
+        table = [self._take() for _ in range(want)]
         for blk in table:
             self.refcount[blk] = 1
         self.tables[seq] = table
@@ -100,7 +104,7 @@ class BlockPoolModel:
             # last block full (or no block yet): one more block at the end
             if not self.free_list:
                 raise PoolError("NOBLOCKS", "no block for growth")
-            blk = self.free_list.popleft()
+            blk = self._take()
             self.refcount[blk] = 1
             table.append(blk)
         elif self.refcount[table[-1]] > 1:
@@ -108,7 +112,7 @@ class BlockPoolModel:
             if not self.free_list:
                 raise PoolError("NOBLOCKS", "no block for copy-on-write")
             src = table[-1]
-            dst = self.free_list.popleft()
+            dst = self._take()
             self.refcount[src] -= 1
             self.refcount[dst] = 1
             table[-1] = dst

@@ -52,6 +52,11 @@ class pa_pool_stats_t(ctypes.Structure):
                 ("tokens", c_i64), ("waste_tokens", c_i64)]
 
 
+class pa_prefix_stats_t(ctypes.Structure):
+    _fields_ = [("lookups", ctypes.c_int64), ("hit_blocks", ctypes.c_int64), ("registered", ctypes.c_int64),
+                ("evictions", ctypes.c_int64), ("cached_blocks", ctypes.c_int32)]
+
+
 class pa_decode_args(ctypes.Structure):
     _fields_ = [("out", c_vp), ("out_dtype", c_i32), ("q", c_vp), ("k_cache", c_vp),
                 ("v_cache", c_vp), ("kv_dtype", c_i32), ("block_tables", c_vp), ("ctx_lens", c_vp),
@@ -93,6 +98,11 @@ _SIGS = {
     "pa_pool_stats": (c_i32, [c_vp, ctypes.POINTER(pa_pool_stats_t)]),
     "pa_pool_refcount": (c_i32, [c_vp, c_i32]),
     "pa_pool_free_list": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
+    "pa_pool_enable_prefix_cache": (c_i32, [c_vp]),
+    "pa_seq_alloc_prefix": (c_i32, [c_vp, c_i64, P_i32, c_i32, ctypes.c_uint64, P_i32, P_i64]),
+    "pa_seq_append_token": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
+    "pa_prefix_cache_stats": (c_i32, [c_vp, ctypes.POINTER(pa_prefix_stats_t)]),
+    "pa_pool_block_cached": (c_i32, [c_vp, c_i32]),
     "pa_write_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_i32, [ctypes.POINTER(pa_decode_args), ctypes.POINTER(c_sz)]),
@@ -223,6 +233,34 @@ class BlockPool:
 
     def refcount(self, block):
         return _lib.pa_pool_refcount(self.handle, block)
+
+    # prefix cache
+    def enable_prefix_cache(self):
+        check(_lib.pa_pool_enable_prefix_cache(self.handle), "pa_pool_enable_prefix_cache")
+
+    def alloc_prefix(self, seq, tokens, salt=0):
+        """Admit seq with its prompt token ids; returns (cached_tokens, slots)."""
+        import numpy as np
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(len(toks), dtype=np.int64)
+        cached = c_i32()
+        check(_lib.pa_seq_alloc_prefix(self.handle, seq, _ptr(toks, c_i32), len(toks), salt, ctypes.byref(cached),
+                                       _ptr(slots, c_i64)), "pa_seq_alloc_prefix")
+        return cached.value, slots
+
+    def append_token(self, seq, token):
+        slot, src, dst = c_i64(), c_i32(), c_i32()
+        check(_lib.pa_seq_append_token(self.handle, seq, int(token), ctypes.byref(slot), ctypes.byref(src),
+                                       ctypes.byref(dst)), "pa_seq_append_token")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def prefix_stats(self):
+        st = pa_prefix_stats_t()
+        check(_lib.pa_prefix_cache_stats(self.handle, ctypes.byref(st)), "pa_prefix_cache_stats")
+        return {f: getattr(st, f) for f, _ in pa_prefix_stats_t._fields_}
+
+    def block_cached(self, block):
+        return _lib.pa_pool_block_cached(self.handle, block)
 
     def free_list(self):
         import numpy as np

@@ -12,8 +12,29 @@
 //   * fork shares blocks by reference count; a write into a still-shared
 //     last block copies it first; full blocks stay shared;
 //   * refused requests change nothing.
-// The free list is a ring buffer of num_blocks entries: it can never hold more
-// ids than there are blocks, so pushes and pops are O(1) without allocation.
+// The free list is an intrusive doubly linked list over the block ids (prev /
+// next arrays): push at the back, pop at the front and removal from the
+// middle (a prefix-cache hit on a free block) are all O(1) without
+// allocation.
+//
+// Optional prefix cache (automatic prefix caching: a full block is identified
+// by its parent block, its tokens and extra keys such as a cache salt, so a
+// new request can find and reuse the blocks of a prefix already in the cache
+// and skip their prefill -- "vllm-pagedattention" (chenyuan1125.github.io),
+// the passage after 一块内存，如何安全地属于多条序列 on automatic prefix caching;
+// a salt keeps tenants' prefixes apart, same page, closing remarks):
+//   * key of a full block = (physical id of its parent block, salt, its B
+//     token ids); a lookup walks a prompt's full blocks from the first and
+//     stops at the first miss;
+//   * a newly full block is registered when its parent is registered (or it
+//     is the first block) and no block holds its key yet;
+//   * a registered block whose count reaches 0 stays cached on the free list;
+//     taking it from the front evicts it (least recently released first); a
+//     hit takes it back off the list;
+//   * with the cache on, a sequence releases its blocks last to first, so a
+//     cached block's cached descendants always sit ahead of it on the free
+//     list and are evicted first: a registered key never names a parent that
+//     has been evicted and reused.
 #include <cstdint>
 #include <new>
 #include <string>
@@ -31,6 +52,37 @@ namespace {
 struct Sequence {
   std::vector<int32_t> table;  // physical block ids, logical order
   int64_t len = 0;             // tokens held
+  // prefix cache: the sequence's token ids are known (admitted with them and
+  // grown token by token); partial holds those of its partly filled last block
+  bool tracked = false;
+  uint64_t salt = 0;
+  std::vector<int32_t> partial;
+};
+
+struct BlockKey {
+  int32_t parent = -1;  // physical id of the parent block, -1 for a first block
+  uint64_t salt = 0;
+  std::vector<int32_t> tokens;
+  bool operator==(const BlockKey& o) const {
+    return parent == o.parent && salt == o.salt && tokens == o.tokens;
+  }
+};
+
+struct BlockKeyHash {
+  size_t operator()(const BlockKey& k) const {
+    // FNV-1a over the parent id, the salt and the tokens (64-bit)
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&h](uint64_t x) {
+      for (int i = 0; i < 8; ++i) {
+        h ^= (x >> (8 * i)) & 0xffu;
+        h *= 1099511628211ull;
+      }
+    };
+    mix(uint64_t(uint32_t(k.parent)));
+    mix(k.salt);
+    for (int32_t t : k.tokens) mix(uint64_t(uint32_t(t)));
+    return size_t(h);
+  }
 };
 
 }  // namespace
@@ -38,21 +90,60 @@ struct Sequence {
 struct pa_pool {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> ring;     // free list storage
-  int64_t head = 0;              // index of the front entry
-  int64_t count = 0;             // entries on the free list
+  std::vector<int32_t> prev, next;  // free list links, -1 at the ends
+  int32_t front = -1, back = -1;
+  int64_t count = 0;                // entries on the free list
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Sequence> seqs;
 
-  int32_t pop_front() {
-    int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
+  // prefix cache
+  bool caching = false;
+  std::unordered_map<BlockKey, int32_t, BlockKeyHash> cache;
+  std::vector<BlockKey> key_of;     // key of each registered block
+  std::vector<char> cached;         // block is registered
+  int64_t lookups = 0, hit_blocks = 0, registered = 0, evictions = 0;
+
+  void unlink(int32_t b) {
+    const int32_t p = prev[b], n = next[b];
+    if (p >= 0) next[p] = n; else front = n;
+    if (n >= 0) prev[n] = p; else back = p;
+    prev[b] = next[b] = -1;
     --count;
+  }
+  int32_t pop_front() {
+    const int32_t b = front;
+    unlink(b);
+    if (cached[b]) {  // a cached block leaving the free list is evicted
+      cache.erase(key_of[b]);
+      key_of[b] = BlockKey();
+      cached[b] = 0;
+      ++evictions;
+    }
     return b;
   }
   void push_back(int32_t b) {
-    ring[(head + count) % num_blocks] = b;
+    prev[b] = back;
+    next[b] = -1;
+    if (back >= 0) next[back] = b; else front = b;
+    back = b;
     ++count;
+  }
+  void release(int32_t b) {
+    if (--refcount[b] == 0) push_back(b);
+  }
+  // Registers block b of a sequence under (parent, salt, tokens) when its
+  // parent is registered (or it is a first block) and the key is new.
+  void try_register(int32_t b, int32_t parent, uint64_t salt, const int32_t* tokens) {
+    if (parent >= 0 && !cached[parent]) return;
+    BlockKey k;
+    k.parent = parent;
+    k.salt = salt;
+    k.tokens.assign(tokens, tokens + block_size);
+    if (cache.count(k)) return;
+    key_of[b] = k;
+    cache.emplace(std::move(k), b);
+    cached[b] = 1;
+    ++registered;
   }
   int64_t slot_of(const Sequence& s, int64_t pos) const {
     return int64_t(s.table[pos / block_size]) * block_size + pos % block_size;
@@ -74,8 +165,11 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
   if (!p) return fail(PA_E_INVAL, "out of host memory");
   p->num_blocks = num_blocks;
   p->block_size = block_size;
-  p->ring.resize(num_blocks);
+  p->prev.assign(num_blocks, -1);
+  p->next.assign(num_blocks, -1);
   p->refcount.assign(num_blocks, 0);
+  p->key_of.resize(num_blocks);
+  p->cached.assign(num_blocks, 0);
   if (initial_free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -85,13 +179,11 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
         return fail(PA_E_INVAL, "initial_free_order is not a permutation of 0..num_blocks-1");
       }
       seen[b] = 1;
-      p->ring[i] = b;
+      p->push_back(b);
     }
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) p->push_back(i);
   }
-  p->head = 0;
-  p->count = num_blocks;
   *out = p;
   return ok();
 }
@@ -138,6 +230,8 @@ pa_status pa_seq_extend(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_ou
   if (grow + (copy ? 1 : 0) > pool->count)
     return fail(PA_E_NOBLOCKS, "need " + std::to_string(grow + (copy ? 1 : 0)) + " blocks, " +
                                    std::to_string(pool->count) + " free");
+  s.tracked = false;  // token ids unknown from here on: no block of s is registered any more
+  s.partial.clear();
   if (copy) {
     int32_t src = s.table.back();
     int32_t dst = pool->pop_front();
@@ -168,6 +262,35 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int64_t* slot_out, int32_t* 
   return st;
 }
 
+pa_status pa_seq_append_token(pa_pool* pool, int64_t seq, int32_t token, int64_t* slot_out,
+                              int32_t* cow_src, int32_t* cow_dst) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  const bool tracked = it->second.tracked;
+  std::vector<int32_t> partial = std::move(it->second.partial);
+  int64_t slot = -1;
+  pa_status st = pa_seq_extend(pool, seq, 1, &slot, cow_src, cow_dst);  // untracks s
+  Sequence& s = pool->seqs.find(seq)->second;
+  if (st != PA_OK) {
+    s.tracked = tracked;
+    s.partial = std::move(partial);
+    return st;
+  }
+  if (slot_out) *slot_out = slot;
+  if (tracked) {
+    s.tracked = true;
+    partial.push_back(token);
+    if (s.len % pool->block_size == 0) {  // the last block just filled up
+      const size_t nb = s.table.size();
+      pool->try_register(s.table[nb - 1], nb >= 2 ? s.table[nb - 2] : -1, s.salt, partial.data());
+      partial.clear();
+    }
+    s.partial = std::move(partial);
+  }
+  return ok();
+}
+
 pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child) {
   if (!pool) return fail(PA_E_INVAL, "pool is null");
   auto it = pool->seqs.find(parent);
@@ -183,11 +306,92 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq) {
   if (!pool) return fail(PA_E_INVAL, "pool is null");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
-  for (int32_t b : it->second.table) {
-    if (--pool->refcount[b] == 0) pool->push_back(b);
+  const std::vector<int32_t>& t = it->second.table;
+  if (pool->caching) {
+    for (size_t i = t.size(); i-- > 0;) pool->release(t[i]);  // last to first
+  } else {
+    for (int32_t b : t) pool->release(b);
   }
   pool->seqs.erase(it);
   return ok();
+}
+
+pa_status pa_pool_enable_prefix_cache(pa_pool* pool) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  if (!pool->seqs.empty()) return fail(PA_E_INVAL, "enable the prefix cache before admitting sequences");
+  pool->caching = true;
+  return ok();
+}
+
+pa_status pa_seq_alloc_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens, int32_t n_tokens,
+                              uint64_t salt, int32_t* cached_tokens_out, int64_t* slots_out) {
+  if (!pool) return fail(PA_E_INVAL, "pool is null");
+  if (!pool->caching) return fail(PA_E_INVAL, "the prefix cache is not enabled on this pool");
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PA_E_INVAL, "n_tokens >= 0 and tokens required");
+  if (pool->seqs.count(seq)) return fail(PA_E_EXISTS, "sequence " + std::to_string(seq));
+  const int32_t B = pool->block_size;
+  const int64_t nfull = n_tokens / B;
+  // Longest cached prefix of whole blocks.
+  std::vector<int32_t> hits;
+  int64_t revive = 0;  // hits that sit on the free list
+  {
+    BlockKey k;
+    k.salt = salt;
+    for (int64_t i = 0; i < nfull; ++i) {
+      k.tokens.assign(tokens + i * B, tokens + (i + 1) * B);
+      ++pool->lookups;
+      auto f = pool->cache.find(k);
+      if (f == pool->cache.end()) break;
+      hits.push_back(f->second);
+      revive += pool->refcount[f->second] == 0;
+      k.parent = f->second;
+    }
+  }
+  const int64_t want = pool->blocks_for(n_tokens) - int64_t(hits.size());
+  if (want > pool->count - revive)
+    return fail(PA_E_NOBLOCKS, "need " + std::to_string(want) + " blocks, " +
+                                   std::to_string(pool->count - revive) + " free");
+  Sequence s;
+  s.table.reserve(pool->blocks_for(n_tokens));
+  for (int32_t b : hits) {
+    if (pool->refcount[b] == 0) pool->unlink(b);
+    pool->refcount[b] += 1;
+    s.table.push_back(b);
+  }
+  for (int64_t i = 0; i < want; ++i) {
+    const int32_t b = pool->pop_front();
+    pool->refcount[b] = 1;
+    s.table.push_back(b);
+  }
+  for (int64_t i = int64_t(hits.size()); i < nfull; ++i)
+    pool->try_register(s.table[i], i > 0 ? s.table[i - 1] : -1, salt, tokens + i * B);
+  pool->hit_blocks += int64_t(hits.size());
+  s.len = n_tokens;
+  s.tracked = true;
+  s.salt = salt;
+  s.partial.assign(tokens + nfull * B, tokens + n_tokens);
+  if (slots_out)
+    for (int64_t i = 0; i < n_tokens; ++i) slots_out[i] = pool->slot_of(s, i);
+  if (cached_tokens_out) *cached_tokens_out = int32_t(hits.size()) * B;
+  pool->seqs.emplace(seq, std::move(s));
+  return ok();
+}
+
+pa_status pa_prefix_cache_stats(const pa_pool* pool, pa_prefix_stats_t* out) {
+  if (!pool || !out) return fail(PA_E_INVAL, "null argument");
+  pa_prefix_stats_t st{};
+  st.lookups = pool->lookups;
+  st.hit_blocks = pool->hit_blocks;
+  st.registered = pool->registered;
+  st.evictions = pool->evictions;
+  st.cached_blocks = int32_t(pool->cache.size());
+  *out = st;
+  return ok();
+}
+
+int32_t pa_pool_block_cached(const pa_pool* pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->cached[block] ? 1 : 0;
 }
 
 pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len_out) {
@@ -245,8 +449,8 @@ int32_t pa_pool_refcount(const pa_pool* pool, int32_t block) {
 
 pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
   if (!pool || !n_out || (cap > 0 && !out) || cap < 0) return fail(PA_E_INVAL, "bad argument");
-  for (int64_t i = 0; i < pool->count && i < cap; ++i)
-    out[i] = pool->ring[(pool->head + i) % pool->num_blocks];
+  int64_t i = 0;
+  for (int32_t b = pool->front; b >= 0 && i < cap; b = pool->next[b]) out[i++] = b;
   *n_out = int32_t(pool->count);
   return ok();
 }
