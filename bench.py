@@ -26,6 +26,7 @@ roofline and oracle baseline.  ``--mode prefill`` prints that object alone.
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -245,6 +246,117 @@ def bench_prefill(steps, warmup, dev, with_cpu):
     return res
 
 
+def bench_prefix(dev, with_cpu, rounds=200, reps=20):
+    """Prefix cache on a batch of 16 requests that share a 1024-token system
+    prompt, each with a private 512-token question (Llama-3.1-8B-like GQA
+    layer, bf16, B = 16).
+    Host: admissions per second through pa_seq_alloc_prefix (each round
+    admits and releases all 16; from the second request on, the system
+    prompt's 64 blocks are found in the cache).
+    GPU: pa_prefill of the batch with the system prompt recomputed (1536-row
+    chunks) and with it cached (512-row chunks over the same 1536-token
+    contexts, through the shared blocks), HIP events around each launch.
+    The oracle model's admissions per second are the CPU baseline."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    S, SYS, Q, B, Hq, Hkv, D = 16, 1024, 512, 16, 32, 8, 128
+    rng = np.random.default_rng(0)
+    system = rng.integers(0, 128000, size=SYS)
+    # every admission brings a question of its own; only the system prompt repeats
+    prompts = [[np.concatenate([system, rng.integers(0, 128000, size=Q)]).astype(np.int32) for _ in range(S)]
+               for _ in range(rounds + 2)]
+    nblocks = S * (SYS + Q) // B + 64
+    pool = P.BlockPool(nblocks, B)
+    pool.enable_prefix_cache()
+
+    def admit_all(p, base, r):
+        return [p.alloc_prefix(base + s, prompts[r][s], salt=7)[0] for s in range(S)]
+
+    admit_all(pool, 0, 0)                  # warm: the system prompt is now cached
+    for s in range(S):
+        pool.free(s)
+    t0 = time.perf_counter()
+    for r in range(rounds):
+        admit_all(pool, (r + 1) * S, r + 1)
+        for s in range(S):
+            pool.free((r + 1) * S + s)
+    host_s = time.perf_counter() - t0
+    st = pool.prefix_stats()
+    cached = admit_all(pool, 10 ** 6, rounds + 1)   # the batch the GPU runs
+    tables, ctx = pool.block_tables([10 ** 6 + s for s in range(S)], (SYS + Q) // B)
+    shared = int(np.sum(tables[:, :SYS // B] == tables[0, :SYS // B]))
+
+    kc = torch.randn((nblocks, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.randn_like(kc)
+    t_tab = torch.from_numpy(tables).to(dev)
+    t_ctx = torch.from_numpy(ctx).to(dev)
+    scale = 1.0 / math.sqrt(D)
+    stream = P.current_stream(dev)
+    times = {}
+    for name, chunk in (("recomputed", SYS + Q), ("cached", Q)):
+        q = torch.randn((S * chunk, Hq, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((S * chunk, Hq, D), dtype=torch.float32, device=dev)
+        qs = torch.arange(0, S * chunk + 1, chunk, dtype=torch.int32, device=dev)
+
+        def call():
+            P.pa_prefill(out, q, kc, vc, t_tab, t_ctx, qs, scale, chunk, stream=stream)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        times[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ctx_l = [SYS + Q] * S
+    flops_cached = prefill_flops(ctx_l, list(range(0, S * Q + 1, Q)), D, Hq)
+    log(f"[bench] prefix cache: {rounds * S / host_s:.0f} admissions/s; prefill recomputed "
+        f"{times['recomputed']:.4f} ms, cached {times['cached']:.4f} ms")
+    res = {
+        "metric": "prefix cache: batch prefill time with a shared system prompt cached vs recomputed",
+        "value": round(times["recomputed"] / times["cached"], 3),
+        "unit": "x (recomputed / cached prefill time)",
+        "config": {"workload": "16 requests, shared 1024-token system prompt + private 512-token questions",
+                   "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "kv_dtype": "bf16",
+                   "cached_tokens_per_request": cached, "system_blocks_shared": shared // S},
+        "prefill_recomputed_ms": round(times["recomputed"], 5),
+        "prefill_cached_ms": round(times["cached"], 5),
+        "host": {"admissions_per_s": round(rounds * S / host_s, 1),
+                 "block_lookups_per_s": round(st["lookups"] / host_s, 1) if host_s > 0 else None,
+                 "hit_blocks": st["hit_blocks"], "registered": st["registered"], "evictions": st["evictions"]},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill, cached (512-row chunks)",
+                     "achieved": round(flops_cached / (times["cached"] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops_cached / (times["cached"] * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        from oracle.prefix_cache import PrefixPoolModel
+        m = PrefixPoolModel(nblocks, B)
+        for s in range(S):
+            m.alloc_prefix(s, prompts[0][s].tolist(), 7)
+        for s in range(S):
+            m.free(s)
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 2.0 and n < rounds:
+            batch = [prompts[n + 1][s].tolist() for s in range(S)]
+            for s in range(S):
+                m.alloc_prefix(10 ** 7 + n * S + s, batch[s], 7)
+            for s in range(S):
+                m.free(10 ** 7 + n * S + s)
+            n += 1
+        wall = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(n * S / wall, 1), "unit": "admissions/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} rounds of 16 admissions + releases, {wall:.1f} s"}
+    return res
+
+
 def copy_calibration(dev):
     """Three plain 1 GiB device copies: the reference for the HBM counters."""
     import torch
@@ -332,8 +444,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "prefill"), default="decode",
-                    help="prefill: print only the pa_prefill measurement")
+    ap.add_argument("--mode", choices=("decode", "prefill", "prefix"), default="decode",
+                    help="prefill / prefix: print only the pa_prefill / prefix-cache measurement")
     ap.add_argument("--no-prefill", action="store_true", help="leave the prefill object out")
     ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -357,6 +469,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.mode == "prefix":
+        res = bench_prefix(dev, not args.no_cpu_baseline)
+        res.update({"n_gpus": 1, "vs_baseline": None})
+        print(json.dumps(res), flush=True)
+        return
     if args.mode == "prefill":
         res = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
         if args.copy_calibration:
@@ -460,6 +577,7 @@ def main():
         result["paged_vs_contiguous"] = comparison
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
+        result["prefix_cache"] = bench_prefix(dev, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)
