@@ -146,6 +146,25 @@ pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len_out);
 pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t n,
                                int32_t max_blocks, int32_t* tables_out, int32_t* ctx_out);
 
+/* Swap-out / swap-in for preemption: a request's blocks are moved to host
+ * memory and back later ("vllm-paged-attention-engine" (aiqz.cc),
+ * 连续批处理：随到随走的新秩序: under memory pressure a request's whole set of
+ * blocks is copied back to CPU memory and copied in again when there is
+ * room).
+ * pa_seq_swap_out writes seq's table (block ids, logical order) to
+ * blocks_out (cap entries; *n_out = their number), releases the blocks as
+ * pa_seq_free would, and marks seq swapped out.  The caller copies those
+ * blocks to host memory (pa_swap_out) on the stream before any later device
+ * write can reach them.  pa_seq_swap_in takes ceil(len / B) fresh blocks
+ * from the front of the free list (all-or-nothing, PA_E_NOBLOCKS), returns
+ * them in logical order and makes seq resident again; the caller copies the
+ * contents back (pa_swap_in).  Blocks shared with other sequences before the
+ * swap come back as private copies.  A swapped-out sequence keeps its id and
+ * length; growth, fork and pa_pool_block_tables refuse it (PA_E_INVAL),
+ * pa_seq_free drops it.  pa_pool_stats counts resident sequences only. */
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq, int32_t* blocks_out, int32_t cap, int32_t* n_out);
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq, int32_t* blocks_out, int32_t cap, int32_t* n_out);
+
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 /* Reference count of a block, or -1 for an id outside [0, num_blocks). */
 int32_t pa_pool_refcount(const pa_pool* pool, int32_t block);
@@ -243,6 +262,24 @@ pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const voi
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int32_t num_blocks, pa_dtype dtype, pa_stream stream);
+
+/* Swap copies for preemption (see pa_seq_swap_out / pa_seq_swap_in):
+ * pa_swap_out copies blocks[0..n) (device int32 ids, the table pa_seq_swap_out
+ * returned) -- every KV head, K and V -- into host, laid out
+ * [n][K, V][num_kv_heads][block_size][head_dim]; pa_swap_in copies such a
+ * buffer back into blocks[0..n) (the table pa_seq_swap_in returned).  host
+ * must be pinned host memory (hipHostMalloc, e.g. a torch pin_memory
+ * tensor; PA_E_INVAL otherwise) of at least 2 * n * block bytes; the kernel
+ * reads or writes it directly over the host link.  Ids outside
+ * [0, num_blocks) are skipped (their host rows are not touched).  Bit copy.
+ * The caller keeps host alive and unchanged until the copy has run
+ * (stream-ordered). */
+pa_status pa_swap_out(const void* k_cache, const void* v_cache, const int32_t* blocks, int32_t n, void* host,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      pa_dtype dtype, pa_stream stream);
+pa_status pa_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n, const void* host,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     pa_dtype dtype, pa_stream stream);
 
 /*
  * Decode attention, one query token per sequence.  For sequence s and query

@@ -36,6 +36,16 @@ Readings taken where the pages are silent:
 * freeing walks the table in order, so released blocks reach the free list
   in table order;
 * the copy-on-write destination is taken from the front of the free list.
+
+Swap-out / swap-in ("vllm-paged-attention-engine" (aiqz.cc), 连续批处理：随到随走的
+新秩序: under memory pressure a request's whole set of blocks is copied back
+to CPU memory, and copied in again when there is room):
+* swap-out hands back the table (the blocks to copy out), releases the blocks
+  as a free would and keeps the sequence's id and length;
+* swap-in takes ceil(len / B) blocks from the front of the free list
+  (all-or-nothing) as the new table; blocks shared before come back private;
+* a swapped-out sequence refuses growth, fork and table views; statistics
+  count resident sequences only.
 """
 from collections import deque
 
@@ -63,6 +73,7 @@ class BlockPoolModel:
         self.refcount = [0] * num_blocks
         self.tables = {}   # seq id -> list of physical block ids
         self.length = {}   # seq id -> tokens held
+        self.swapped = set()
 
     # -- helpers -----------------------------------------------------------
     def _take(self):
@@ -76,6 +87,18 @@ class BlockPoolModel:
     def _need(self, seq):
         if seq not in self.tables:
             raise PoolError("NOSEQ", f"unknown sequence {seq}")
+
+    def _resident(self, seq):
+        self._need(seq)
+        if seq in self.swapped:
+            raise PoolError("INVAL", f"sequence {seq} is swapped out")
+
+    def _release(self, table):
+        """Blocks whose count reaches zero go to the back, in table order."""
+        for blk in table:
+            self.refcount[blk] -= 1
+            if self.refcount[blk] == 0:
+                self.free_list.append(blk)
 
     # -- verbs -------------------------------------------------------------
     def alloc(self, seq, n_tokens):
@@ -96,7 +119,7 @@ class BlockPoolModel:
 
     def append(self, seq):
         """Reserve the next token's slot; returns (slot, cow pair or None)."""
-        self._need(seq)
+        self._resident(seq)
         table = self.tables[seq]
         pos = self.length[seq]
         cow = None
@@ -125,6 +148,7 @@ class BlockPoolModel:
         self._need(parent)
         if child in self.tables:
             raise PoolError("EXISTS", f"sequence {child} exists")
+        self._resident(parent)
         table = list(self.tables[parent])
         for blk in table:
             self.refcount[blk] += 1
@@ -134,15 +158,37 @@ class BlockPoolModel:
     def free(self, seq):
         """Drop ``seq``; blocks whose count reaches zero return to the back."""
         self._need(seq)
-        for blk in self.tables.pop(seq):
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.free_list.append(blk)
+        self._release(self.tables.pop(seq))
         del self.length[seq]
+        self.swapped.discard(seq)
+
+    def swap_out(self, seq):
+        """Release seq's blocks, keep its id and length; returns the old table."""
+        self._resident(seq)
+        table = self.tables[seq]
+        self._release(table)
+        self.tables[seq] = []
+        self.swapped.add(seq)
+        return list(table)
+
+    def swap_in(self, seq):
+        """Fresh blocks for a swapped-out seq; returns the new table."""
+        self._need(seq)
+        if seq not in self.swapped:
+            raise PoolError("INVAL", f"sequence {seq} is not swapped out")
+        want = -(-self.length[seq] // self.block_size)
+        if want > len(self.free_list):
+            raise PoolError("NOBLOCKS", f"need {want}, have {len(self.free_list)}")
+        table = [self._take() for _ in range(want)]
+        for blk in table:
+            self.refcount[blk] = 1
+        self.tables[seq] = table
+        self.swapped.discard(seq)
+        return list(table)
 
     # -- views -------------------------------------------------------------
     def block_table(self, seq):
-        self._need(seq)
+        self._resident(seq)
         return list(self.tables[seq])
 
     def seq_len(self, seq):
@@ -163,8 +209,8 @@ class BlockPoolModel:
     def stats(self):
         used = sum(1 for c in self.refcount if c > 0)
         shared = sum(1 for c in self.refcount if c > 1)
-        tokens = sum(self.length.values())
-        waste = sum(len(self.tables[s]) * self.block_size - self.length[s]
-                    for s in self.tables)
+        resident = [s for s in self.tables if s not in self.swapped]
+        tokens = sum(self.length[s] for s in resident)
+        waste = sum(len(self.tables[s]) * self.block_size - self.length[s] for s in resident)
         return {"free": len(self.free_list), "used": used, "shared": shared,
-                "seqs": len(self.tables), "tokens": tokens, "waste_tokens": waste}
+                "seqs": len(resident), "tokens": tokens, "waste_tokens": waste}

@@ -116,7 +116,7 @@ class PrefixPoolModel(BlockPoolModel):
 
     def append_token(self, seq, token):
         """Growth by one token whose id is known: (slot, cow pair or None)."""
-        self._need(seq)
+        self._resident(seq)
         tracked = seq in self.tokens
         slot, cow = BlockPoolModel.append(self, seq)
         if tracked:
@@ -139,15 +139,18 @@ class PrefixPoolModel(BlockPoolModel):
             self.tokens[child] = list(self.tokens[parent])
             self.salt[child] = self.salt[parent]
 
+    def _release(self, table):
+        """With the cache on, blocks go back last to first."""
+        super()._release(list(reversed(table)))
+
     def free(self, seq):
-        """Drop seq; blocks go back last to first."""
-        self._need(seq)
-        for blk in reversed(self.tables.pop(seq)):
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.free_list.append(blk)
-        del self.length[seq]
+        super().free(seq)
         self._untrack(seq)
+
+    def swap_out(self, seq):
+        table = super().swap_out(seq)
+        self._untrack(seq)           # blocks restored by swap-in are not registered
+        return table
 
     # -- views ---------------------------------------------------------------
     def prefix_stats(self):

@@ -98,6 +98,8 @@ _SIGS = {
     "pa_pool_stats": (c_i32, [c_vp, ctypes.POINTER(pa_pool_stats_t)]),
     "pa_pool_refcount": (c_i32, [c_vp, c_i32]),
     "pa_pool_free_list": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
+    "pa_seq_swap_out": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
+    "pa_seq_swap_in": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
     "pa_pool_enable_prefix_cache": (c_i32, [c_vp]),
     "pa_seq_alloc_prefix": (c_i32, [c_vp, c_i64, P_i32, c_i32, ctypes.c_uint64, P_i32, P_i64]),
     "pa_seq_append_token": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
@@ -105,6 +107,8 @@ _SIGS = {
     "pa_pool_block_cached": (c_i32, [c_vp, c_i32]),
     "pa_write_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_swap_out": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_swap_in": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_i32, [ctypes.POINTER(pa_decode_args), ctypes.POINTER(c_sz)]),
     "pa_decode": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
     "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
@@ -234,6 +238,25 @@ class BlockPool:
     def refcount(self, block):
         return _lib.pa_pool_refcount(self.handle, block)
 
+    # swap
+    def swap_out(self, seq):
+        """Release seq's blocks (it stays known, swapped out); returns them in table order."""
+        import numpy as np
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = c_i32()
+        check(_lib.pa_seq_swap_out(self.handle, seq, _ptr(out, c_i32), self.num_blocks, ctypes.byref(n)),
+              "pa_seq_swap_out")
+        return out[:n.value].copy()
+
+    def swap_in(self, seq):
+        """Fresh blocks for a swapped-out seq; returns them in table order."""
+        import numpy as np
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = c_i32()
+        check(_lib.pa_seq_swap_in(self.handle, seq, _ptr(out, c_i32), self.num_blocks, ctypes.byref(n)),
+              "pa_seq_swap_in")
+        return out[:n.value].copy()
+
     # prefix cache
     def enable_prefix_cache(self):
         check(_lib.pa_pool_enable_prefix_cache(self.handle), "pa_pool_enable_prefix_cache")
@@ -306,6 +329,33 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
     check(_lib.pa_copy_blocks(_dev(k_cache), _dev(v_cache), _dev(pairs) if n else None, n, hkv, d, B,
                               nb, DTYPE_OF[k_cache.dtype],
                               stream if stream is not None else current_stream()), "pa_copy_blocks")
+
+
+def _swap(fn, k_cache, v_cache, blocks, host, stream):
+    nb, hkv, B, d = _cache_dims(k_cache)
+    if blocks.dtype != torch.int32:
+        raise ValueError("blocks must be int32")
+    _dev(k_cache), _dev(v_cache), _dev(blocks)
+    if host.device.type != "cpu" or not host.is_pinned():
+        raise ValueError("host must be a pinned CPU tensor (pin_memory=True)")
+    n = blocks.numel()
+    need = 2 * n * hkv * B * d * k_cache.element_size()
+    if host.numel() * host.element_size() < need or not host.is_contiguous():
+        raise ValueError(f"host must be a contiguous buffer of at least {need} bytes")
+    check(fn(k_cache.data_ptr(), v_cache.data_ptr(), blocks.data_ptr(), n, host.data_ptr(), hkv, d, B, nb,
+             DTYPE_OF[k_cache.dtype], stream if stream is not None else current_stream(k_cache.device)),
+          fn.__name__)
+
+
+def pa_swap_out(k_cache, v_cache, blocks, host, stream=None):
+    """Copy blocks (device int32 ids) of both caches into the pinned host
+    buffer, laid out [n][K, V][Hkv][B][d]."""
+    _swap(_lib.pa_swap_out, k_cache, v_cache, blocks, host, stream)
+
+
+def pa_swap_in(k_cache, v_cache, blocks, host, stream=None):
+    """Copy a pinned host buffer laid out as pa_swap_out writes it back into blocks."""
+    _swap(_lib.pa_swap_in, k_cache, v_cache, blocks, host, stream)
 
 
 def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,

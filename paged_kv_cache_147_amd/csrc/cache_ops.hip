@@ -10,6 +10,8 @@
 // writes whole 128-byte lines.
 #include "device_common.h"
 
+#include <algorithm>
+
 namespace pkv {
 namespace {
 
@@ -51,6 +53,28 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   uint4* to = reinterpret_cast<uint4*>(cache + int64_t(dst) * block_bytes);
   const int64_t n = block_bytes / 16;
   for (int64_t i = threadIdx.x; i < n; i += kThreads) to[i] = from[i];
+}
+
+// Swap copies (preemption: a request's blocks go to host memory and come
+// back later, "vllm-paged-attention-engine" (aiqz.cc), 连续批处理：随到随走的新秩序).
+// Workgroup (i, half, part) moves part `part` of the K (half 0) or V (half 1)
+// bytes of block blocks[i] between the caches and the host buffer, laid out
+// [n][K, V][block bytes]; 16-byte loads and stores, consecutive lanes on
+// consecutive bytes, so each wave moves 1 KB contiguous over the link.  Ids
+// outside [0, num_blocks) are skipped.
+__global__ __launch_bounds__(kThreads) void swap_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                        char* __restrict__ host, const int32_t* __restrict__ blocks,
+                                                        int64_t block_bytes, int32_t num_blocks, int32_t to_host) {
+  const int32_t b = blocks[blockIdx.x];
+  if (b < 0 || b >= num_blocks) return;
+  char* cache = (blockIdx.y == 0 ? kc : vc) + int64_t(b) * block_bytes;
+  char* h = host + (int64_t(blockIdx.x) * 2 + blockIdx.y) * block_bytes;
+  const int64_t n = block_bytes / 16;
+  const int64_t per = (n + gridDim.z - 1) / gridDim.z;
+  const int64_t lo = per * blockIdx.z, hi = min(n, lo + per);
+  uint4* dst = reinterpret_cast<uint4*>(to_host ? h : cache);
+  const uint4* srcp = reinterpret_cast<const uint4*>(to_host ? cache : h);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) dst[i] = srcp[i];
 }
 
 pa_status check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -104,4 +128,45 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
                      static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), pairs, block_bytes, num_blocks);
   return launch_status("copy_blocks kernel");
+}
+
+namespace {
+
+pa_status launch_swap(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n, const void* host,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      pa_dtype dtype, pa_stream stream, bool to_host) {
+  pa_status st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (n < 0) return fail(PA_E_INVAL, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!k_cache || !v_cache || !blocks || !host) return fail(PA_E_INVAL, "null pointer");
+  // the kernel reaches the host buffer through its device-side address,
+  // which exists for pinned (hipHostMalloc) memory only
+  void* dev_host = nullptr;
+  if (hipHostGetDevicePointer(&dev_host, const_cast<void*>(host), 0) != hipSuccess || !dev_host) {
+    (void)hipGetLastError();
+    return fail(PA_E_INVAL, "host buffer is not pinned host memory (hipHostMalloc)");
+  }
+  const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * dtype_bytes(dtype);
+  const unsigned parts = unsigned(std::max<int64_t>(1, block_bytes / (kThreads * 16 * 4)));  // 4 rounds per workgroup
+  hipLaunchKernelGGL(swap_kernel, dim3(unsigned(n), 2, parts), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), static_cast<char*>(dev_host), blocks,
+                     block_bytes, num_blocks, to_host ? 1 : 0);
+  return launch_status("swap kernel");
+}
+
+}  // namespace
+
+extern "C" pa_status pa_swap_out(const void* k_cache, const void* v_cache, const int32_t* blocks, int32_t n,
+                                 void* host, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype dtype, pa_stream stream) {
+  return launch_swap(const_cast<void*>(k_cache), const_cast<void*>(v_cache), blocks, n, host, num_kv_heads,
+                     head_dim, block_size, num_blocks, dtype, stream, true);
+}
+
+extern "C" pa_status pa_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_t n, const void* host,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                pa_dtype dtype, pa_stream stream) {
+  return launch_swap(k_cache, v_cache, blocks, n, host, num_kv_heads, head_dim, block_size, num_blocks, dtype,
+                     stream, false);
 }

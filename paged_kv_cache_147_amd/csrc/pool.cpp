@@ -57,6 +57,8 @@ struct Sequence {
   bool tracked = false;
   uint64_t salt = 0;
   std::vector<int32_t> partial;
+  // swapped out: the contents live in host memory, the sequence holds no block
+  bool swapped = false;
 };
 
 struct BlockKey {
@@ -130,6 +132,15 @@ struct pa_pool {
   }
   void release(int32_t b) {
     if (--refcount[b] == 0) push_back(b);
+  }
+  // Gives back a sequence's blocks: in table order, or last to first with the
+  // prefix cache on (descendants then reach the free list first).
+  void release_table(const std::vector<int32_t>& t) {
+    if (caching) {
+      for (size_t i = t.size(); i-- > 0;) release(t[i]);
+    } else {
+      for (int32_t b : t) release(b);
+    }
   }
   // Registers block b of a sequence under (parent, salt, tokens) when its
   // parent is registered (or it is a first block) and the key is new.
@@ -221,6 +232,7 @@ pa_status pa_seq_extend(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_ou
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
   Sequence& s = it->second;
+  if (s.swapped) return fail(PA_E_INVAL, "sequence " + std::to_string(seq) + " is swapped out");
   if (n == 0) return ok();
   const int32_t B = pool->block_size;
   // Blocks this request takes: one copy if the first token lands in a shared,
@@ -267,6 +279,7 @@ pa_status pa_seq_append_token(pa_pool* pool, int64_t seq, int32_t token, int64_t
   if (!pool) return fail(PA_E_INVAL, "pool is null");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  if (it->second.swapped) return fail(PA_E_INVAL, "sequence " + std::to_string(seq) + " is swapped out");
   const bool tracked = it->second.tracked;
   std::vector<int32_t> partial = std::move(it->second.partial);
   int64_t slot = -1;
@@ -296,6 +309,7 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child) {
   auto it = pool->seqs.find(parent);
   if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "parent " + std::to_string(parent));
   if (pool->seqs.count(child)) return fail(PA_E_EXISTS, "child " + std::to_string(child));
+  if (it->second.swapped) return fail(PA_E_INVAL, "parent " + std::to_string(parent) + " is swapped out");
   Sequence c = it->second;  // copy of table and length
   for (int32_t b : c.table) pool->refcount[b] += 1;
   pool->seqs.emplace(child, std::move(c));
@@ -306,13 +320,47 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq) {
   if (!pool) return fail(PA_E_INVAL, "pool is null");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
-  const std::vector<int32_t>& t = it->second.table;
-  if (pool->caching) {
-    for (size_t i = t.size(); i-- > 0;) pool->release(t[i]);  // last to first
-  } else {
-    for (int32_t b : t) pool->release(b);
-  }
+  pool->release_table(it->second.table);  // empty when swapped out
   pool->seqs.erase(it);
+  return ok();
+}
+
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq, int32_t* blocks_out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out) return fail(PA_E_INVAL, "null argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  Sequence& s = it->second;
+  if (s.swapped) return fail(PA_E_INVAL, "sequence " + std::to_string(seq) + " is already swapped out");
+  const int64_t nb = int64_t(s.table.size());
+  if (nb > cap || (nb > 0 && !blocks_out)) return fail(PA_E_INVAL, "blocks_out holds fewer entries than the table");
+  for (int64_t i = 0; i < nb; ++i) blocks_out[i] = s.table[i];
+  *n_out = int32_t(nb);
+  pool->release_table(s.table);
+  s.table.clear();
+  s.swapped = true;
+  s.tracked = false;  // blocks restored by swap-in are not registered
+  s.partial.clear();
+  return ok();
+}
+
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq, int32_t* blocks_out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out) return fail(PA_E_INVAL, "null argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seq));
+  Sequence& s = it->second;
+  if (!s.swapped) return fail(PA_E_INVAL, "sequence " + std::to_string(seq) + " is not swapped out");
+  const int64_t want = pool->blocks_for(s.len);
+  if (want > cap || (want > 0 && !blocks_out)) return fail(PA_E_INVAL, "blocks_out holds fewer entries than the table");
+  if (want > pool->count)
+    return fail(PA_E_NOBLOCKS, "need " + std::to_string(want) + " blocks, " + std::to_string(pool->count) + " free");
+  for (int64_t i = 0; i < want; ++i) {
+    const int32_t b = pool->pop_front();
+    pool->refcount[b] = 1;
+    s.table.push_back(b);
+    blocks_out[i] = b;
+  }
+  *n_out = int32_t(want);
+  s.swapped = false;
   return ok();
 }
 
@@ -411,6 +459,7 @@ pa_status pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end()) return fail(PA_E_NOSEQ, "sequence " + std::to_string(seqs[i]));
     const Sequence& s = it->second;
+    if (s.swapped) return fail(PA_E_INVAL, "sequence " + std::to_string(seqs[i]) + " is swapped out");
     if (int64_t(s.table.size()) > max_blocks)
       return fail(PA_E_INVAL, "sequence " + std::to_string(seqs[i]) + " holds " +
                                   std::to_string(s.table.size()) + " blocks > max_blocks");
@@ -433,8 +482,9 @@ pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out) {
     st.used_blocks += c > 0;
     st.shared_blocks += c > 1;
   }
-  st.num_seqs = int32_t(pool->seqs.size());
-  for (const auto& kv : pool->seqs) {
+  for (const auto& kv : pool->seqs) {  // resident sequences (swapped ones hold no block)
+    if (kv.second.swapped) continue;
+    st.num_seqs += 1;
     st.tokens += kv.second.len;
     st.waste_tokens += int64_t(kv.second.table.size()) * pool->block_size - kv.second.len;
   }

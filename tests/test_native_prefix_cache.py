@@ -36,7 +36,7 @@ def run_log(seed, num_blocks, B, steps):
     systems = [list(rng.integers(0, 50, size=int(rng.integers(B, 5 * B)))) for _ in range(3)]
     live, next_id = [], 0
     for _ in range(steps):
-        op = rng.choice(["admit", "admit", "token", "token", "token", "fork", "free", "plain"])
+        op = rng.choice(["admit", "admit", "token", "token", "token", "fork", "free", "plain", "swap"])
         if op == "admit" or not live:
             sys_p = systems[int(rng.integers(0, len(systems)))]
             cut = int(rng.integers(0, len(sys_p) + 1))
@@ -80,6 +80,20 @@ def run_log(seed, num_blocks, B, steps):
             native.fork(s, next_id)
             live.append(next_id)
             next_id += 1
+        elif op == "swap":
+            # swap a sequence out, and (if the pool has room) straight back in
+            s = live[int(rng.integers(0, len(live)))]
+            assert list(native.swap_out(s)) == model.swap_out(s)
+            try:
+                exp = model.swap_in(s)
+            except PoolError:
+                with pytest.raises(P.PagedKVError):
+                    native.swap_in(s)
+                live.remove(s)
+                model.free(s)
+                native.free(s)
+            else:
+                assert list(native.swap_in(s)) == exp
         else:
             s = live.pop(int(rng.integers(0, len(live))))
             model.free(s)
