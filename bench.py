@@ -357,6 +357,87 @@ def bench_prefix(dev, with_cpu, rounds=200, reps=20):
     return res
 
 
+PCIE5_X16_GBPS = 64.0   # one direction, nominal
+
+
+def bench_swap(dev, with_cpu, seqs=64, tokens=2048, reps=5):
+    """Swap copies: preempting `seqs` sequences of `tokens` tokens of the
+    Llama-3.1-8B-like GQA layer (8 KV heads, head_dim 128, bf16, B = 16):
+    their blocks, scattered over a pool, go to pinned host memory
+    (pa_swap_out) and come back into other scattered blocks (pa_swap_in).
+    HIP events around each launch; beside them a plain contiguous copy of the
+    same bytes between the device and the same pinned buffer (the practical
+    ceiling of the host link).  CPU baseline: the layout definition written
+    out in numpy (a gather of the same blocks from a host copy of the
+    caches)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    Hkv, B, D = 8, 16, 128
+    nblk = seqs * tokens // B
+    pool_blocks = 2 * nblk + 64
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(pool_blocks).astype(np.int32)
+    out_ids = torch.from_numpy(perm[:nblk].copy()).to(dev)
+    in_ids = torch.from_numpy(perm[nblk:2 * nblk].copy()).to(dev)
+    kc = torch.randn((pool_blocks, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.randn_like(kc)
+    host = torch.empty((nblk, 2, Hkv, B, D), dtype=torch.bfloat16).pin_memory()
+    nbytes = host.numel() * host.element_size()
+    flat = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    stream = P.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    hflat = host.view(-1)
+    t_out = timed(lambda: P.pa_swap_out(kc, vc, out_ids, host, stream=stream))
+    t_in = timed(lambda: P.pa_swap_in(kc, vc, in_ids, host, stream=stream))
+    t_d2h = timed(lambda: hflat.copy_(flat, non_blocking=True))
+    t_h2d = timed(lambda: flat.copy_(hflat, non_blocking=True))
+    ok = bool(torch.equal(kc[in_ids.long()].view(torch.int16), kc[out_ids.long()].view(torch.int16)))
+    gb = nbytes / 1e9
+    log(f"[bench] swap: out {t_out:.3f} ms ({gb / t_out * 1e3:.1f} GB/s), in {t_in:.3f} ms "
+        f"({gb / t_in * 1e3:.1f} GB/s); plain copies {gb / t_d2h * 1e3:.1f} / {gb / t_h2d * 1e3:.1f} GB/s")
+    res = {
+        "metric": "swap-out / swap-in of preempted sequences' blocks: GB/s over the host link",
+        "value": round(gb / t_out * 1e3, 2),
+        "unit": "GB/s (swap-out)",
+        "config": {"workload": f"{seqs} sequences x {tokens} tokens, Llama-3.1-8B-like GQA layer",
+                   "num_kv_heads": Hkv, "block_size": B, "head_dim": D, "kv_dtype": "bf16", "blocks": nblk,
+                   "bytes": nbytes, "blocks_scattered_over": pool_blocks},
+        "swap_out_ms": round(t_out, 4), "swap_in_ms": round(t_in, 4),
+        "swap_in_gbps": round(gb / t_in * 1e3, 2),
+        "plain_copy_gbps": {"device_to_host": round(gb / t_d2h * 1e3, 2), "host_to_device": round(gb / t_h2d * 1e3, 2)},
+        "round_trip_bit_exact": ok,
+        "roofline": {"bound": "pcie", "kernel": "pa_swap_out (one launch)", "achieved": round(gb / t_out * 1e3, 2),
+                     "peak": PCIE5_X16_GBPS, "unit": "GB/s", "frac": round(gb / t_out * 1e3 / PCIE5_X16_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        kh, vh = kc.view(torch.int16).cpu().numpy(), vc.view(torch.int16).cpu().numpy()
+        ids = out_ids.cpu().numpy()
+        dst = np.empty((nblk, 2, Hkv, B, D), dtype=np.int16)
+        t0 = time.perf_counter()
+        dst[:, 0] = kh[ids]
+        dst[:, 1] = vh[ids]
+        wall = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(gb / wall, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"numpy gather of the same {nblk} blocks into the documented layout, "
+                                         f"host memory to host memory, {wall:.2f} s"}
+    return res
+
+
 def copy_calibration(dev):
     """Three plain 1 GiB device copies: the reference for the HBM counters."""
     import torch
@@ -444,7 +525,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "prefill", "prefix"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "prefill", "prefix", "swap"), default="decode",
                     help="prefill / prefix: print only the pa_prefill / prefix-cache measurement")
     ap.add_argument("--no-prefill", action="store_true", help="leave the prefill object out")
     ap.add_argument("--prefill-steps", type=int, default=50)
@@ -469,6 +550,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.mode == "swap":
+        res = bench_swap(dev, not args.no_cpu_baseline)
+        res.update({"n_gpus": 1, "vs_baseline": None})
+        print(json.dumps(res), flush=True)
+        return
     if args.mode == "prefix":
         res = bench_prefix(dev, not args.no_cpu_baseline)
         res.update({"n_gpus": 1, "vs_baseline": None})
@@ -578,6 +664,7 @@ def main():
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
         result["prefix_cache"] = bench_prefix(dev, not args.no_cpu_baseline)
+        result["swap"] = bench_swap(dev, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)
