@@ -55,6 +55,12 @@ typedef int32_t pa_dtype;
 #define PA_F32 0
 #define PA_F16 1
 #define PA_BF16 2
+/* One-byte E4M3 codes of a quantised KV cache (OCP 8-bit float, "FN": 1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7F / 0xFF NaN,
+ * no infinities, largest finite 448), each cache with one float32 scale:
+ * element = value(code) * scale.  Cache dtype only: written by
+ * pa_write_kv_fp8, read by pa_decode, moved by the bit-copy calls. */
+#define PA_FP8_E4M3 3
 
 typedef void* pa_stream; /* a hipStream_t */
 
@@ -238,7 +244,9 @@ int32_t pa_pool_block_cached(const pa_pool* pool, int32_t block);
  * of block_size * head_dim elements is contiguous, so a block is contiguous
  * inside and blocks sit anywhere ("Paged Attention", 定义).
  * Supported set: head_dim in {64, 128}; block_size in {8, 16, 32};
- * dtype in {PA_F32, PA_F16, PA_BF16}.
+ * dtype in {PA_F32, PA_F16, PA_BF16}, and PA_FP8_E4M3 for the bit copies
+ * (pa_write_kv of codes, pa_copy_blocks, pa_swap_*), pa_write_kv_fp8 and
+ * pa_decode.
  */
 
 /* Scatter num_tokens new tokens into their slots ("vllm-pagedattention",
@@ -253,6 +261,23 @@ pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const voi
                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
                       pa_dtype dtype, pa_stream stream);
+
+/* Quantising scatter into an E4M3 cache (PA_FP8_E4M3 layout above).  Same
+ * slots and skipping rules as pa_write_kv; k_new, v_new hold src_dtype
+ * values (PA_F32, PA_F16 or PA_BF16).  Each element x is stored as the E4M3
+ * code nearest to y = x * r, r = 1 / k_scale (v_scale for V) rounded to
+ * float32 once and the product rounded to float32: ties go to the even code,
+ * |y| >= 448 saturates to +-448, NaN gives 0x7F.  Scales must be finite and
+ * positive (PA_E_INVAL otherwise).  Quantised caches are one lever on the
+ * cache's byte floor besides fewer KV heads and shorter contexts
+ * ("Paged Attention" (daiw.org), 量化, the boxed warning); serving systems
+ * ship FP8 caches ("vLLM PagedAttention：大模型推理的显存管理革命", 生态现状).
+ * The pages fix no format; E4M3 with a per-cache scale is this library's
+ * choice. */
+pa_status pa_write_kv_fp8(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          pa_dtype src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          float k_scale, float v_scale, pa_stream stream);
 
 /* Copy-on-write block copies ("vllm-pagedattention", 一块内存…: the shared last
  * block is copied before the branch writes).  pairs: n_pairs x 2 int32 device
@@ -338,7 +363,18 @@ typedef struct pa_decode_args {
   void* workspace;             /* device scratch, >= pa_decode_workspace_bytes,
                                   256-byte aligned */
   size_t workspace_bytes;
+  /* E4M3 caches (kv_dtype PA_FP8_E4M3) only; ignored otherwise: */
+  pa_dtype q_dtype;            /* PA_F16 or PA_BF16: q's dtype; out_dtype is PA_F32 or q_dtype */
+  float k_scale;               /* finite, > 0: K element = value(code) * k_scale */
+  float v_scale;               /* finite, > 0 */
 } pa_decode_args;
+/*
+ * E4M3 caches: head_dim 128, fixed partitions only (partition_size >= 0).
+ * Codes are widened exactly to q_dtype, q.K and p.V run on the matrix cores
+ * with float32 accumulation (p as a 16-bit value plus the 16-bit rounding of
+ * its remainder), k_scale is folded into the score scale and v_scale into
+ * the weighted sums.
+ */
 /*
  * Device-side data: a ctx_lens entry <= 0 yields a zero output row; entries
  * above max_ctx are clamped to it (the caller guarantees they do not occur);

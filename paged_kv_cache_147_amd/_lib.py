@@ -15,11 +15,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_E_INVAL, PA_E_NOBLOCKS, PA_E_NOSEQ, PA_E_EXISTS, PA_E_UNSUPPORTED, PA_E_HIP = 0, -1, -2, -3, -4, -5, -6
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 STATUS_NAMES = {0: "OK", -1: "INVAL", -2: "NOBLOCKS", -3: "NOSEQ", -4: "EXISTS", -5: "UNSUPPORTED",
                 -6: "HIP"}
 TORCH_DTYPE = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
 DTYPE_OF = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+# E4M3 caches: torch's float8_e4m3fn (the same encoding) or raw uint8 codes
+DTYPE_OF.update({torch.float8_e4m3fn: PA_FP8_E4M3, torch.uint8: PA_FP8_E4M3})
 NAME_OF = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 
@@ -63,7 +65,8 @@ class pa_decode_args(ctypes.Structure):
                 ("num_seqs", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
                 ("head_dim", c_i32), ("block_size", c_i32), ("max_blocks", c_i32),
                 ("num_blocks", c_i32), ("max_ctx", c_i32), ("scale", c_f32),
-                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz),
+                ("q_dtype", c_i32), ("k_scale", c_f32), ("v_scale", c_f32)]
 
 
 class pa_contig_args(ctypes.Structure):
@@ -106,6 +109,8 @@ _SIGS = {
     "pa_prefix_cache_stats": (c_i32, [c_vp, ctypes.POINTER(pa_prefix_stats_t)]),
     "pa_pool_block_cached": (c_i32, [c_vp, c_i32]),
     "pa_write_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_write_kv_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
+                                c_f32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_swap_out": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_swap_in": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
@@ -320,6 +325,28 @@ def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
                            stream if stream is not None else current_stream()), "pa_write_kv")
 
 
+def pa_write_kv_fp8(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantise [T][Hkv][d] rows (float32 / float16 / bfloat16) to E4M3 codes
+    in the caches (uint8 or float8_e4m3fn) at ``slot_mapping`` (int64)."""
+    nb, hkv, B, d = _cache_dims(k_cache)
+    if DTYPE_OF.get(k_cache.dtype) != PA_FP8_E4M3 or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must be uint8 or float8_e4m3fn")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    T = slot_mapping.numel()
+    if k_new.shape != (T, hkv, d) or v_new.shape != (T, hkv, d) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [T][Hkv][d] of one dtype")
+    src = DTYPE_OF.get(k_new.dtype)
+    if src not in (PA_F32, PA_F16, PA_BF16):
+        raise ValueError("k_new / v_new must be float32, float16 or bfloat16")
+    for t in (k_cache, v_cache, k_new, v_new, slot_mapping):
+        _dev(t)
+    check(_lib.pa_write_kv_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), src,
+                               slot_mapping.data_ptr(), T, hkv, d, B, nb, float(k_scale), float(v_scale),
+                               stream if stream is not None else current_stream(k_cache.device)),
+          "pa_write_kv_fp8")
+
+
 def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
     """Copy whole blocks for each (src, dst) row of the int32 ``pairs`` [n][2]."""
     nb, hkv, B, d = _cache_dims(k_cache)
@@ -359,7 +386,7 @@ def pa_swap_in(k_cache, v_cache, blocks, host, stream=None):
 
 
 def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
-                partition_size=0, workspace=None):
+                partition_size=0, workspace=None, k_scale=1.0, v_scale=1.0):
     nb, hkv, B, d = _cache_dims(k_cache)
     S, hq, dq = q.shape
     a = pa_decode_args()
@@ -381,6 +408,8 @@ def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.q_dtype = DTYPE_OF.get(q.dtype, -1)
+    a.k_scale, a.v_scale = k_scale, v_scale
     return a
 
 
@@ -398,15 +427,17 @@ def workspace_for(nbytes, device):
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
-              partition_size=0, workspace=None, stream=None):
-    """Paged decode attention into ``out`` ([S][Hq][d], float32 or the cache dtype)."""
+              partition_size=0, workspace=None, stream=None, k_scale=1.0, v_scale=1.0):
+    """Paged decode attention into ``out`` ([S][Hq][d], float32 or the cache
+    dtype; float32 or q's dtype for E4M3 caches, whose scales are k_scale and
+    v_scale)."""
     for t, dt in ((block_tables, torch.int32), (ctx_lens, torch.int32)):
         if t.dtype != dt:
             raise ValueError("block_tables and ctx_lens must be int32")
     for t in (out, q, k_cache, v_cache, block_tables, ctx_lens):
         _dev(t)
     a = decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx, partition_size,
-                    workspace)
+                    workspace, k_scale, v_scale)
     if workspace is None:
         need = pa_decode_workspace_bytes(a)
         if need:

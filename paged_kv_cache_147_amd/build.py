@@ -23,11 +23,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # Device code: gfx950 only; packed float32 ops stay off (ordinary float code
 # is compiled to unpacked VALU instructions).
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["status.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["status.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "decode_fp8.hip", "prefill.hip"]
 # Per-source extras.  prefill: matrix-core accumulators in ordinary VGPRs, so
 # the softmax can rescale them in place (in AGPRs every step would copy them
 # out and back).
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():

@@ -11,6 +11,7 @@
 #include "device_common.h"
 
 #include <algorithm>
+#include <cmath>
 
 namespace pkv {
 namespace {
@@ -77,9 +78,67 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(char* __restrict__ kc, c
   for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) dst[i] = srcp[i];
 }
 
+// E4M3 code ("FN": no infinities, largest finite 448) of a float32: the
+// nearest code, ties to the even code, magnitudes >= 448 saturate to +-448,
+// NaN gives 0x7F.  Exact integer work on the float32 bits.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;              // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;      // |y| >= 448 = 1.75 * 2^8
+  const int e = int(a >> 23) - 127;               // exponent of |y|
+  if (e < -6) {                                   // below the smallest normal 2^-6:
+    // steps of 2^-9; |y| * 512 < 8 is exact, rint rounds ties to even; 8 is
+    // code 0x08, the smallest normal
+    return sign | uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  }
+  uint32_t q = (a & 0x7fffffu) >> 20;             // 3 mantissa bits, then round the other 20
+  const uint32_t rest = a & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) q += 1;   // a carry moves into the exponent
+  return sign | ((uint32_t(e + 7) << 3) + q);
+}
+
+// pa_write_kv_fp8: each thread quantises 16 consecutive elements of one new
+// row (16 bytes of E4M3 out), x * inv_scale in float32 first.
+template <class T>
+__global__ __launch_bounds__(kThreads) void write_kv_fp8_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const char* __restrict__ kn, const char* __restrict__ vn,
+    const int64_t* __restrict__ slots, int64_t groups_per_token, int32_t groups_per_row, int32_t head_dim,
+    int32_t block_size, int64_t num_slots, int64_t total, float k_inv, float v_inv) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= 2 * total) return;
+  const bool is_v = i >= total;
+  const int64_t j = is_v ? i - total : i;
+  const int64_t tok = j / groups_per_token;
+  const int64_t rem = j % groups_per_token;              // (head, group) within the token
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t head = rem / groups_per_row, grp = rem % groups_per_row;
+  const int64_t num_kv_heads = groups_per_token / groups_per_row;
+  const char* src = (is_v ? vn : kn) + ((tok * num_kv_heads + head) * head_dim + grp * 16) * T::bytes;
+  const float inv = is_v ? v_inv : k_inv;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float x;
+      if constexpr (T::bytes == 4) x = reinterpret_cast<const float*>(src)[4 * q + b];
+      else x = widen1(T{}, reinterpret_cast<const uint16_t*>(src)[4 * q + b]);
+      word |= e4m3_code(x * inv) << (8 * b);
+    }
+    w[q] = word;
+  }
+  const int64_t blk = slot / block_size, row = slot % block_size;
+  uint8_t* dst = (is_v ? vc : kc) + ((blk * num_kv_heads + head) * block_size + row) * head_dim + grp * 16;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 pa_status check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int32_t num_blocks, pa_dtype dtype) {
-  if (!valid_dtype(dtype)) return fail(PA_E_UNSUPPORTED, "dtype");
+                            int32_t num_blocks, pa_dtype dtype, bool codes_ok = true) {
+  if (!(codes_ok ? valid_storage_dtype(dtype) : valid_dtype(dtype))) return fail(PA_E_UNSUPPORTED, "dtype");
   if (num_kv_heads <= 0 || num_blocks <= 0) return fail(PA_E_INVAL, "num_kv_heads and num_blocks must be positive");
   if (head_dim != 64 && head_dim != 128) return fail(PA_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (block_size != 8 && block_size != 16 && block_size != 32)
@@ -169,4 +228,35 @@ extern "C" pa_status pa_swap_in(void* k_cache, void* v_cache, const int32_t* blo
                                 pa_dtype dtype, pa_stream stream) {
   return launch_swap(k_cache, v_cache, blocks, n, host, num_kv_heads, head_dim, block_size, num_blocks, dtype,
                      stream, false);
+}
+
+extern "C" pa_status pa_write_kv_fp8(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                     pa_dtype src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float k_scale, float v_scale, pa_stream stream) {
+  pa_status st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, src_dtype, false);
+  if (st != PA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_E_INVAL, "k_scale and v_scale must be finite and positive");
+  if (num_tokens < 0) return fail(PA_E_INVAL, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return fail(PA_E_INVAL, "null device pointer");
+  const int32_t groups_per_row = head_dim / 16;
+  const int64_t groups_per_token = int64_t(num_kv_heads) * groups_per_row;
+  const int64_t total = groups_per_token * num_tokens;
+  const int64_t grid = (2 * total + kThreads - 1) / kThreads;
+  if (grid > INT32_MAX) return fail(PA_E_INVAL, "too many tokens for one launch");
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;   // rounded to float32 once, on the host
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto go = [&](auto tag) {
+    hipLaunchKernelGGL(write_kv_fp8_kernel<decltype(tag)>, dim3(unsigned(grid)), dim3(kThreads), 0, hs,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), slot_mapping,
+                       groups_per_token, groups_per_row, head_dim, block_size, int64_t(num_blocks) * block_size,
+                       total, k_inv, v_inv);
+  };
+  if (src_dtype == PA_F32) go(F32{});
+  else if (src_dtype == PA_F16) go(F16{});
+  else go(BF16{});
+  return launch_status("write_kv_fp8 kernel");
 }

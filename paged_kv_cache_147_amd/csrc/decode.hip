@@ -35,6 +35,7 @@
 // next is in flight, and the first V rows are requested before the softmax.
 // Block ids of a partition are fetched once, one per lane, and broadcast
 // with readlane, so each pass's base address is a scalar.
+#include "decode_params.h"
 #include "device_common.h"
 
 #include <algorithm>
@@ -207,44 +208,10 @@ __device__ __forceinline__ void store_run(T, uint16_t* o, const float* a, float 
 
 // ---- kernels ----------------------------------------------------------------
 
-// Header of the balanced schedule, written by decode_plan_kernel.
-struct Sched {
-  int64_t total;           // tiles over all (KV head, sequence) ranges
-  int32_t tiles_per_head;  // tiles over all sequences of one KV head
-  int32_t pieces;          // pieces (= waves with work); 0 when there is no context
-};
 constexpr int kTile = 16;             // tokens per schedule tile
 constexpr int kMinTilesPerPiece = 8;  // fewer pieces than waves when the batch is small
 constexpr int kMaxWaves = 8192;       // pieces the workspace is sized for, at most
 
-struct DecodeParams {
-  void* out;
-  const void* q;
-  const char* k;
-  const char* v;
-  const int32_t* tables;
-  const int32_t* ctx_lens;
-  float* part_o;        // fixed: [S][Hq][num_parts][D]; balanced: [2 pieces][G][D] unnormalised sums
-  float* part_ml;       // same rows, (max, sum of weights) in the log2 domain
-  Sched* sched;         // balanced: schedule header
-  int32_t* cum;         // balanced: [S + 1] tiles of the sequences before s (per KV head)
-  int32_t* start_seq;   // balanced: [pieces] sequence holding each piece's first tile
-  int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
-  int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
-  int32_t num_seqs;
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t block_size;
-  int32_t log2_block;
-  int32_t max_blocks;
-  int32_t num_blocks;
-  int32_t max_ctx;
-  int32_t part_tokens;  // fixed: partition length; balanced: chunk length
-  int32_t num_parts;
-  int32_t num_waves;    // balanced: upper bound on pieces (waves launched, rounded up to 8)
-  int32_t out_f32;
-  float scale_log2e;    // scale * log2(e): scores live in the log2 domain
-};
 
 // q.K on the matrix cores: for a GQA group (G >= 2) of 16-bit heads, the
 // scores of 16 tokens x G heads are a small dense contraction over head_dim,
@@ -309,33 +276,6 @@ __device__ __forceinline__ f32x4_t mfma_qk(F16, uint4 a, uint4 b, f32x4_t c) {
 // waves: the oldest wave issues first, so of four equal pieces on one SIMD
 // the first finishes in about half the time of the last.
 
-// Linear workgroup id -> (KV head, sequence, partition), fixed partitions.
-// * KV head varies fastest: consecutive workgroups go to the 8 XCDs in turn,
-//   so with Hkv a multiple of 8 each XCD serves a fixed set of KV heads for
-//   every sequence and all XCDs get the same work.
-// * Sequences are taken in chunks of kSeqChunk; inside a chunk, partition
-//   varies slowest.  Sequences that share prefix blocks (forks, beams) sit
-//   next to each other, so their reads of the same (block, head) tile happen
-//   at about the same time on the same XCD and hit its L2, while the working
-//   set of a chunk stays within that L2.
-// * Partitions past a sequence's end exit at once; they fall at the end of
-//   each chunk rather than on particular XCDs.
-constexpr int kSeqChunk = 32;
-struct Unit { int g, s, part; };
-__device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
-  Unit u;
-  u.g = id % p.num_kv_heads;
-  const int rest = id / p.num_kv_heads;
-  const int chunk = rest / (kSeqChunk * p.num_parts);
-  const int within = rest % (kSeqChunk * p.num_parts);
-  u.part = within / kSeqChunk;
-  u.s = chunk * kSeqChunk + within % kSeqChunk;
-  if (u.s >= p.num_seqs) {  // padding of the last chunk: an empty unit
-    u.s = 0;
-    u.part = p.num_parts;
-  }
-  return u;
-}
 
 // Piece k of the balanced schedule covers flattened tiles
 // [piece_start(k), piece_start(k + 1)); piece_of(pos) is the piece holding
@@ -1204,9 +1144,20 @@ pa_status check_paged(const pa_decode_args* a, Plan* plan) {
   if (a->max_ctx < 0 || a->max_ctx > table_ctx)
     return fail(PA_E_INVAL, "max_ctx must be in [0, max_blocks * block_size]");
   const int bound = a->max_ctx ? a->max_ctx : int(table_ctx);
-  return plan_decode(a->num_seqs, a->num_q_heads, a->num_kv_heads, a->head_dim, a->kv_dtype,
+  pa_dtype compute = a->kv_dtype;
+  if (a->kv_dtype == PA_FP8_E4M3) {
+    if (a->q_dtype != PA_F16 && a->q_dtype != PA_BF16)
+      return fail(PA_E_UNSUPPORTED, "E4M3 caches need q_dtype PA_F16 or PA_BF16");
+    if (a->head_dim != 128) return fail(PA_E_UNSUPPORTED, "E4M3 caches need head_dim 128");
+    if (a->partition_size < 0) return fail(PA_E_UNSUPPORTED, "E4M3 caches use fixed partitions (partition_size >= 0)");
+    if (!(a->k_scale > 0.f) || !(a->v_scale > 0.f) || !std::isfinite(a->k_scale) || !std::isfinite(a->v_scale))
+      return fail(PA_E_INVAL, "k_scale and v_scale must be finite and positive");
+    compute = a->q_dtype;
+  }
+  return plan_decode(a->num_seqs, a->num_q_heads, a->num_kv_heads, a->head_dim, compute,
                      a->out_dtype, a->block_size, bound, a->partition_size, a->scale, plan);
 }
+
 
 pa_status check_contig(const pa_contig_args* a, Plan* plan) {
   if (!a) return fail(PA_E_INVAL, "args is null");
@@ -1329,7 +1280,20 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   p.num_parts = plan.num_parts;
   p.out_f32 = a->out_dtype == PA_F32;
   p.scale_log2e = a->scale * 1.4426950408889634f;
-  return launch<true>(p, plan, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,
+  p.v_scale = 1.f;
+  const int G = a->num_q_heads / a->num_kv_heads;
+  if (a->kv_dtype == PA_FP8_E4M3) {
+    p.scale_log2e = float(double(a->scale) * double(a->k_scale) * 1.4426950408889634);
+    p.v_scale = a->v_scale;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = launch_decode_fp8_partitions(p, a->q_dtype, G, hs);
+    if (st != PA_OK || p.num_parts <= 1) return st;
+    const dim3 combine_grid(unsigned(int64_t(a->num_seqs) * a->num_q_heads));
+    if (a->q_dtype == PA_F16) hipLaunchKernelGGL((decode_combine_kernel<F16, 128, false>), combine_grid, dim3(kWave), 0, hs, p);
+    else hipLaunchKernelGGL((decode_combine_kernel<BF16, 128, false>), combine_grid, dim3(kWave), 0, hs, p);
+    return launch_status("decode combine kernel");
+  }
+  return launch<true>(p, plan, a->kv_dtype, a->head_dim, G, a->num_seqs,
                       a->num_kv_heads, static_cast<hipStream_t>(stream));
 }
 

@@ -1,0 +1,83 @@
+// Internal: the parameter block of the decode kernels and the fixed-partition
+// unit mapping, shared by the 16-bit / float32 kernels and the E4M3 kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+// Header of the balanced schedule, written by decode_plan_kernel.
+struct Sched {
+  int64_t total;           // tiles over all (KV head, sequence) ranges
+  int32_t tiles_per_head;  // tiles over all sequences of one KV head
+  int32_t pieces;          // pieces (= waves with work); 0 when there is no context
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const char* k;
+  const char* v;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* part_o;        // fixed: [S][Hq][num_parts][D]; balanced: [2 pieces][G][D] unnormalised sums
+  float* part_ml;       // same rows, (max, sum of weights) in the log2 domain
+  Sched* sched;         // balanced: schedule header
+  int32_t* cum;         // balanced: [S + 1] tiles of the sequences before s (per KV head)
+  int32_t* start_seq;   // balanced: [pieces] sequence holding each piece's first tile
+  int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
+  int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t log2_block;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_ctx;
+  int32_t part_tokens;  // fixed: partition length; balanced: chunk length
+  int32_t num_parts;
+  int32_t num_waves;    // balanced: upper bound on pieces (waves launched, rounded up to 8)
+  int32_t out_f32;
+  float scale_log2e;    // scale * log2(e) (times k_scale for E4M3 caches): scores live in the log2 domain
+  float v_scale;        // E4M3 caches: V element = value(code) * v_scale
+};
+
+// Linear workgroup id -> (KV head, sequence, partition), fixed partitions.
+// * KV head varies fastest: consecutive workgroups go to the 8 XCDs in turn,
+//   so with Hkv a multiple of 8 each XCD serves a fixed set of KV heads for
+//   every sequence and all XCDs get the same work.
+// * Sequences are taken in chunks of kSeqChunk; inside a chunk, partition
+//   varies slowest.  Sequences that share prefix blocks (forks, beams) sit
+//   next to each other, so their reads of the same (block, head) tile happen
+//   at about the same time on the same XCD and hit its L2, while the working
+//   set of a chunk stays within that L2.
+// * Partitions past a sequence's end exit at once; they fall at the end of
+//   each chunk rather than on particular XCDs.
+constexpr int kSeqChunk = 32;
+struct Unit { int g, s, part; };
+__device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
+  Unit u;
+  u.g = id % p.num_kv_heads;
+  const int rest = id / p.num_kv_heads;
+  const int chunk = rest / (kSeqChunk * p.num_parts);
+  const int within = rest % (kSeqChunk * p.num_parts);
+  u.part = within / kSeqChunk;
+  u.s = chunk * kSeqChunk + within % kSeqChunk;
+  if (u.s >= p.num_seqs) {  // padding of the last chunk: an empty unit
+    u.s = 0;
+    u.part = p.num_parts;
+  }
+  return u;
+}
+
+// Launches decode_fp8_kernel over the fixed-partition grid (E4M3 caches,
+// head_dim 128, q of type q_dtype, G query heads per KV head); the caller
+// launches the combine kernel when contexts span several partitions.
+pa_status launch_decode_fp8_partitions(const DecodeParams& p, pa_dtype q_dtype, int G, hipStream_t st);
+
+}  // namespace pkv

@@ -19,10 +19,12 @@ struct F16 { static constexpr int bytes = 2; };
 struct BF16 { static constexpr int bytes = 2; };
 
 inline int dtype_bytes(pa_dtype t) {
-  return t == PA_F32 ? 4 : (t == PA_F16 || t == PA_BF16) ? 2 : 0;
+  return t == PA_F32 ? 4 : (t == PA_F16 || t == PA_BF16) ? 2 : t == PA_FP8_E4M3 ? 1 : 0;
 }
 
+// Types the kernels compute with; E4M3 codes are a cache storage type only.
 inline bool valid_dtype(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+inline bool valid_storage_dtype(pa_dtype t) { return valid_dtype(t) || t == PA_FP8_E4M3; }
 
 // float32 -> 16-bit, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t narrow(F16, float x) {

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 def declared():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():
@@ -31,7 +31,7 @@ def test_header_declares_expected_entry_points():
 def test_every_declared_symbol_is_exported_and_bound():
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (pa_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT (pa_[a-z0-9_]+)$", out, flags=re.M))
     names = declared()
     missing = [n for n in names if n not in exported]
     assert not missing, missing
