@@ -19,9 +19,13 @@ prefill over the paged cache) on the Llama-3.1-8B-like prefill batch (16
 sequences, 512-token chunks after cached prefixes of 0..2048 tokens), in
 algorithmic TFLOP/s against the dense bf16 matrix-core peak, with its own
 roofline and oracle baseline.  ``--mode prefill`` prints that object alone.
+``prefix_cache`` and ``swap`` measure the prefix cache and the preemption
+copies; ``fp8`` runs the same decode step over an E4M3 copy of the cache
+(pa_write_kv_fp8 of the new tokens, pa_decode over codes), with its own
+roofline and oracle baseline.  ``--mode prefix|swap|fp8`` prints one alone.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--mode decode|prefill] [--no-prefill]
+                    [--mode decode|prefill|prefix|swap|fp8] [--no-prefill]
 """
 import argparse
 import hashlib
@@ -71,7 +75,7 @@ def decode_bytes(wl, ctx):
     return kv, kv + other
 
 
-def source_digest(names=("decode.hip", "device_common.h")):
+def source_digest(names=("decode.hip", "decode_params.h", "device_common.h")):
     h = hashlib.sha256()
     for name in names:
         with open(os.path.join(ROOT, "paged_kv_cache_147_amd", "csrc", name), "rb") as f:
@@ -438,6 +442,149 @@ def bench_swap(dev, with_cpu, seqs=64, tokens=2048, reps=5):
     return res
 
 
+FP8_METRIC = "paged decode attention over an E4M3 (FP8) KV cache: KV HBM GB/s (% of MI355X peak)"
+FP8_TRAFFIC_WORKLOAD = "llama31_8b_gqa_fp8"
+
+
+def measured_fp8_traffic(workload):
+    """Per-launch HBM bytes of the E4M3 decode from the committed counter
+    summary, or None when its source changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    m = re.search(r"^\|\s*" + re.escape(workload) + r"\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.e+]+)\s*\|",
+                  text, flags=re.M)
+    if not m or m.group(1) != source_digest(("decode_fp8.hip", "decode_params.h", "device_common.h")):
+        return None
+    return float(m.group(2))
+
+
+def fp8_cpu_baseline(wl, k_scale, v_scale, budget_s=10.0):
+    """oracle.fp8.paged_decode_fp8, as it stands, on the first sequences of the
+    batch until ~budget_s of work (codes quantised by the oracle beforehand,
+    untimed); scaled to GB/s of code bytes."""
+    import numpy as np
+
+    from oracle import fp8 as F
+    from oracle.bits import to_f64
+    from tests._replay import OracleRun
+    run = OracleRun(wl)
+    tables, lens = run.tables(wl)
+    kc = F.quantize(to_f64(run.cache.k, wl.dtype).astype(np.float32), k_scale)
+    vc = F.quantize(to_f64(run.cache.v, wl.dtype).astype(np.float32), v_scale)
+    done, kv, wall, cpu = 0, 0, 0.0, 0.0
+    while done < wl.num_seqs and wall < budget_s:
+        n = min(8, wl.num_seqs - done)
+        sl = slice(done, done + n)
+        t0, c0 = time.perf_counter(), time.process_time()
+        F.paged_decode_fp8(wl.q[sl], wl.dtype, kc, vc, k_scale, v_scale, tables[sl], lens[sl], wl.block_size,
+                           wl.scale, wl.num_q_heads, wl.num_kv_heads)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        kv += int(np.sum(lens[sl])) * 2 * wl.num_kv_heads * wl.head_dim
+        done += n
+    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB of codes), "
+                      f"{wall:.1f} s wall, float64 numpy",
+            "seqs_per_s": round(done / wall, 2)}
+
+
+def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, with_cpu, bf16_decode_ms=None,
+              k_scale=1 / 56, v_scale=1 / 72, partition_size=0):
+    """The decode step over an E4M3 cache: the bf16 cache of the same batch is
+    quantised once (pa_write_kv_fp8 over every slot, untimed), then each step
+    runs the copy-on-write copies, pa_write_kv_fp8 of the new tokens and
+    pa_decode over the codes; pa_decode is timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    nb, hkv, B, d = run.k_cache.shape
+    stream = P.current_stream(dev)
+    rows_k = run.k_cache.permute(0, 2, 1, 3).reshape(nb * B, hkv, d).contiguous()
+    rows_v = run.v_cache.permute(0, 2, 1, 3).reshape(nb * B, hkv, d).contiguous()
+    all_slots = torch.arange(nb * B, dtype=torch.int64, device=dev)
+    kc = torch.empty((nb, hkv, B, d), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    P.pa_write_kv_fp8(kc, vc, rows_k, rows_v, all_slots, k_scale, v_scale, stream=stream)
+    del rows_k, rows_v
+    replicas = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(nrep - 1)]
+    ctx = run.ctx_host.tolist()
+    step_rows = torch.cat([torch.arange(r0, r0 + n) for (_, r0, n) in run.step_writes]).to(dev)
+    step_slots = torch.cat([sl for (sl, _, _) in run.step_writes])
+    k_new = run.k_rows.index_select(0, step_rows).contiguous()
+    v_new = run.v_rows.index_select(0, step_rows).contiguous()
+    pairs = torch.tensor(run.step_copies, dtype=torch.int32, device=dev) if run.step_copies else None
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    probe = P._lib.decode_args(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=max(ctx),
+                               partition_size=partition_size, k_scale=k_scale, v_scale=v_scale)
+    ws = P._lib.workspace_for(P.pa_decode_workspace_bytes(probe), dev)
+
+    def step(i, ev=None):
+        k, v = replicas[i % len(replicas)]
+        if pairs is not None:
+            P.pa_copy_blocks(k, v, pairs, stream=stream)
+        P.pa_write_kv_fp8(k, v, k_new, v_new, step_slots, k_scale, v_scale, stream=stream)
+        if ev is not None:
+            ev[0].record()
+        P.pa_decode(out, run.q, k, v, run.tables, run.ctx, wl.scale, max_ctx=max(ctx), workspace=ws,
+                    partition_size=partition_size, stream=stream, k_scale=k_scale, v_scale=v_scale)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = elapsed * 1e3 / steps
+    dec_avg = float(np.mean(dec_ms))
+    S, Hq = wl.num_seqs, wl.num_q_heads
+    kv = int(sum(ctx)) * 2 * hkv * d
+    alg = kv + S * Hq * d * 2 + S * Hq * d * 4 + sum(4 * ((c + B - 1) // B) for c in ctx) + 4 * S
+    log(f"[bench] fp8: {steps} steps: {ms_step:.4f} ms/step; pa_decode avg {dec_avg:.4f} ms "
+        f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
+    gbps = kv / (ms_step * 1e-3) / 1e9
+    achieved = alg / (dec_avg * 1e-3) / 1e9
+    res = {
+        "metric": FP8_METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "dtype": "fp8_e4m3 codes, bf16 q, f32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": workload + "_fp8", "batch": S, "num_q_heads": Hq, "num_kv_heads": hkv,
+                   "head_dim": d, "block_size": B, "kv_dtype": "fp8_e4m3", "q_dtype": wl.dtype,
+                   "out_dtype": "f32", "k_scale": k_scale, "v_scale": v_scale, "partition_size": partition_size,
+                   "ctx_mean": round(float(np.mean(ctx)), 1), "kv_bytes_per_step": kv,
+                   "cache_replicas": len(replicas)},
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "seqs_per_s": round(S / (ms_step * 1e-3), 1),
+        "decode_speedup_vs_bf16": round(bf16_decode_ms / dec_avg, 3) if bf16_decode_ms else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_fp8_traffic(workload + "_fp8"),
+                     "kernel": "pa_decode over E4M3 codes (partition + combine launches)",
+                     "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg,
+                     "launch_ms_p10_median_p90": [round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)]},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        log("[bench] timing the E4M3 oracle on a CPU sample ...")
+        res["cpu_baseline"] = fp8_cpu_baseline(wl, k_scale, v_scale)
+    return res
+
+
 def copy_calibration(dev):
     """Three plain 1 GiB device copies: the reference for the HBM counters."""
     import torch
@@ -525,9 +672,10 @@ def main():
     ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "prefill", "prefix", "swap"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "prefill", "prefix", "swap", "fp8"), default="decode",
                     help="prefill / prefix: print only the pa_prefill / prefix-cache measurement")
-    ap.add_argument("--no-prefill", action="store_true", help="leave the prefill object out")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave the prefill, prefix-cache, swap and fp8 objects out")
     ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -575,6 +723,14 @@ def main():
     ctx = run.ctx_host.tolist()
     kv_bytes, alg_bytes = decode_bytes(wl, ctx)
     log(f"[bench] cache built; {wl.num_seqs} seqs, KV {kv_bytes / 1e9:.3f} GB logical")
+    if args.mode == "fp8":
+        res = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas,
+                        not args.no_cpu_baseline, partition_size=args.partition_size)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        res.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
+        print(json.dumps(res), flush=True)
+        return
 
     # The step's own work: copies, then one write of every new token.
     step_rows = torch.cat([torch.arange(r0, r0 + n) for (_, r0, n) in run.step_writes]).to(dev)
@@ -665,6 +821,8 @@ def main():
         result["prefill"] = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
         result["prefix_cache"] = bench_prefix(dev, not args.no_cpu_baseline)
         result["swap"] = bench_swap(dev, not args.no_cpu_baseline)
+        result["fp8"] = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas,
+                                  not args.no_cpu_baseline, bf16_decode_ms=dec_avg)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -46,6 +46,9 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr float kFp8Slack = 8.f;
+// Word 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data
+// format, no swizzle; loads through it are plain byte-addressed loads.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -66,18 +69,24 @@ __device__ __forceinline__ f32x4_t mfma(F16, u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 // Two E4M3 codes (bytes 0 and 1 of w, or 2 and 3 when HI) -> their values as
-// two packed 16-bit floats of type T.  The hardware conversion to float32 is
-// exact; so is dropping the low half of those float32s (bfloat16) or
-// converting them to float16, since the values fit both formats.
+// two packed 16-bit floats of type T, in one gfx950 conversion with a scale
+// of 1 (every E4M3 value is exactly a float16 and a bfloat16 value; checked
+// on all byte pairs, NaN codes give NaN).  Issued as inline assembly: the
+// compiler's own model of this instruction's two result halves has been
+// seen to merge them wrongly when one half is extracted.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3_pair(BF16, uint32_t w) {
-  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), HI);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+  uint32_t r;
+  if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return r;
 }
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3_pair(F16, uint32_t w) {
-  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), HI);
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  uint32_t r;
+  if constexpr (HI) asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  else asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return r;
 }
 
 // Bytes of two rows' words a (row e) and b (row e + 1), regrouped into token
@@ -177,18 +186,51 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
       return (k < 8 ? base : base2) + (k & 7) * ROW;
     }
   };
-  auto load = [&](Fp8Rows& b, int st) {
+  // Blocks of >= 16 tokens: a span is 16 consecutive rows of one block, read
+  // as buffer loads from a scalar resource over those 2 KB plus a fixed lane
+  // offset and an immediate (no per-lane address arithmetic).
+  const uint32_t koff = uint32_t(m16) * ROW + 16u * q4;          // K: row m16, bytes 16 q4 (+64)
+  const uint32_t voff = uint32_t(4 * q4) * ROW + 8u * m16;       // V: row 4 q4 (+j), bytes 8 m16
+  // Loads are issued for every step of the double-buffered loop, also the
+  // one past the last: it gets a resource of zero bytes, so it moves nothing
+  // and returns zeros, and the wait counts stay the same on every path (a
+  // load under a branch would make the compiler drain all loads instead).
+  auto span_rsrc = [&](const char* cache, int tb, bool live) {
+    const int lb = min((tb >> p.log2_block) - b0, lb_last);
+    const int phys = __builtin_amdgcn_readlane(lane_block, lb);
+    const char* base = cache + (int64_t(phys) * p.num_kv_heads + g) * p.tile_bytes +
+                       int64_t(tb & (p.block_size - 1)) * ROW;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? 16 * ROW : 0, kRawBufferWord3);
+  };
+  auto load = [&](Fp8Rows& b, int st_in) {
+    const bool live = st_in < nsteps;
+    const int st = min(st_in, nsteps - 1);
     const int t0 = tok0 + 32 * st;
+    if constexpr (!SPLIT) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const char* r = row_ptr(p.k, t0 + 16 * h, m16);
-      b.k[h][0] = *reinterpret_cast<const uint4*>(r + 16 * q4);
-      b.k[h][1] = *reinterpret_cast<const uint4*>(r + 64 + 16 * q4);
-    }
+      for (int h = 0; h < 2; ++h) {
+        const auto rk = span_rsrc(p.k, t0 + 16 * h, live);
+        b.k[h][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0));
+        b.k[h][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64, 0, 0));
+        const auto rv = span_rsrc(p.v, t0 + 16 * h, live);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b.v[j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0, 4 * q4 + j) + 8 * m16);
-      b.v[4 + j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0 + 16, 4 * q4 + j) + 8 * m16);
+        for (int j = 0; j < 4; ++j)
+          b.v[4 * h + j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + j * ROW, 0, 0));
+      }
+    } else {
+      // two blocks per span: per-lane addresses; a step past the last
+      // re-reads the last step's rows (cached) instead
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* r = row_ptr(p.k, t0 + 16 * h, m16);
+        b.k[h][0] = *reinterpret_cast<const uint4*>(r + 16 * q4);
+        b.k[h][1] = *reinterpret_cast<const uint4*>(r + 64 + 16 * q4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b.v[j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0, 4 * q4 + j) + 8 * m16);
+        b.v[4 + j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0 + 16, 4 * q4 + j) + 8 * m16);
+      }
     }
   };
 
@@ -291,16 +333,24 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
     else compute(b, st, std::false_type{});
   };
 
+  // The scheduling barriers keep every buffer's loads in the same order in
+  // the prologue and the loop, so the waits before a buffer is used count
+  // only its own loads (loads issued in another order on one path would make
+  // the compiler drain everything at the loop head).
   Fp8Rows bufA, bufB;
   load(bufA, 0);
-  if (nsteps > 1) load(bufB, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load(bufB, 1);
+  __builtin_amdgcn_sched_barrier(0);
   for (int st = 0; st < nsteps; st += 2) {
     step(bufA, st);
-    if (st + 2 < nsteps) load(bufA, st + 2);
-    if (st + 1 < nsteps) {
-      step(bufB, st + 1);
-      if (st + 3 < nsteps) load(bufB, st + 3);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    load(bufA, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nsteps) step(bufB, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(bufB, st + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Lane (m16, q4) holds head m16's columns 32 q4 + 8 i + nn in o[nn][i].
