@@ -369,7 +369,7 @@ typedef struct pa_decode_args {
   float v_scale;               /* finite, > 0 */
 } pa_decode_args;
 /*
- * E4M3 caches: head_dim 128, fixed partitions only (partition_size >= 0).
+ * E4M3 caches: fixed partitions only (partition_size >= 0).
  * Codes are widened exactly to q_dtype, q.K and p.V run on the matrix cores
  * with float32 accumulation (p as a 16-bit value plus the 16-bit rounding of
  * its remainder), k_scale is folded into the score scale and v_scale into

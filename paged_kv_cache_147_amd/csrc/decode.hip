@@ -1148,7 +1148,6 @@ pa_status check_paged(const pa_decode_args* a, Plan* plan) {
   if (a->kv_dtype == PA_FP8_E4M3) {
     if (a->q_dtype != PA_F16 && a->q_dtype != PA_BF16)
       return fail(PA_E_UNSUPPORTED, "E4M3 caches need q_dtype PA_F16 or PA_BF16");
-    if (a->head_dim != 128) return fail(PA_E_UNSUPPORTED, "E4M3 caches need head_dim 128");
     if (a->partition_size < 0) return fail(PA_E_UNSUPPORTED, "E4M3 caches use fixed partitions (partition_size >= 0)");
     if (!(a->k_scale > 0.f) || !(a->v_scale > 0.f) || !std::isfinite(a->k_scale) || !std::isfinite(a->v_scale))
       return fail(PA_E_INVAL, "k_scale and v_scale must be finite and positive");
@@ -1286,11 +1285,17 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
     p.scale_log2e = float(double(a->scale) * double(a->k_scale) * 1.4426950408889634);
     p.v_scale = a->v_scale;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = launch_decode_fp8_partitions(p, a->q_dtype, G, hs);
+    st = launch_decode_fp8_partitions(p, a->q_dtype, a->head_dim, G, hs);
     if (st != PA_OK || p.num_parts <= 1) return st;
-    const dim3 combine_grid(unsigned(int64_t(a->num_seqs) * a->num_q_heads));
-    if (a->q_dtype == PA_F16) hipLaunchKernelGGL((decode_combine_kernel<F16, 128, false>), combine_grid, dim3(kWave), 0, hs, p);
-    else hipLaunchKernelGGL((decode_combine_kernel<BF16, 128, false>), combine_grid, dim3(kWave), 0, hs, p);
+    const dim3 cg(unsigned(int64_t(a->num_seqs) * a->num_q_heads));
+    const bool d64 = a->head_dim == 64;
+    if (a->q_dtype == PA_F16) {
+      if (d64) hipLaunchKernelGGL((decode_combine_kernel<F16, 64, false>), cg, dim3(kWave), 0, hs, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<F16, 128, false>), cg, dim3(kWave), 0, hs, p);
+    } else {
+      if (d64) hipLaunchKernelGGL((decode_combine_kernel<BF16, 64, false>), cg, dim3(kWave), 0, hs, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<BF16, 128, false>), cg, dim3(kWave), 0, hs, p);
+    }
     return launch_status("decode combine kernel");
   }
   return launch<true>(p, plan, a->kv_dtype, a->head_dim, G, a->num_seqs,

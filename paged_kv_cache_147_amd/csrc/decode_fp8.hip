@@ -130,19 +130,21 @@ __device__ __forceinline__ float fp8_sum_xor32(float x) {
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-// One step's rows in registers: K of both tiles (two 16-byte pieces each) and
-// the lane's 8 V rows.
+// One step's rows in registers: K of both tiles (D / 64 16-byte pieces each)
+// and D / 16 bytes of each of the lane's 8 V rows.
+template <int D>
 struct Fp8Rows {
-  uint4 k[2][2];
-  uint2 v[8];
+  uint4 k[2][D / 64];
+  uint2 v[8];  // .y unused when D == 64
 };
 
 // SPLIT: 8-token blocks, so a 16-token span covers two blocks.
-template <class T, int G, bool SPLIT>
+template <class T, int D, int G, bool SPLIT>
 __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int KK = D / 32;  // score MFMA steps
-  constexpr int NN = D / 16;  // output column blocks
+  constexpr int NN = D / 16;  // output column blocks = V bytes per lane and row
+  constexpr int KP = D / 64;  // 16-byte K pieces per lane and row
   constexpr int ROW = D;      // bytes per cached row
   const int lane = threadIdx.x, m16 = lane & 15, q4 = lane >> 4;
   const Unit unit = unit_of(blockIdx.x, p);
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
   // as buffer loads from a scalar resource over those 2 KB plus a fixed lane
   // offset and an immediate (no per-lane address arithmetic).
   const uint32_t koff = uint32_t(m16) * ROW + 16u * q4;          // K: row m16, bytes 16 q4 (+64)
-  const uint32_t voff = uint32_t(4 * q4) * ROW + 8u * m16;       // V: row 4 q4 (+j), bytes 8 m16
+  const uint32_t voff = uint32_t(4 * q4) * ROW + uint32_t(NN) * m16;  // V: row 4 q4 (+j), bytes NN m16
   // Loads are issued for every step of the double-buffered loop, also the
   // one past the last: it gets a resource of zero bytes, so it moves nothing
   // and returns zeros, and the wait counts stay the same on every path (a
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
                        int64_t(tb & (p.block_size - 1)) * ROW;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? 16 * ROW : 0, kRawBufferWord3);
   };
-  auto load = [&](Fp8Rows& b, int st_in) {
+  auto load = [&](Fp8Rows<D>& b, int st_in) {
     const bool live = st_in < nsteps;
     const int st = min(st_in, nsteps - 1);
     const int t0 = tok0 + 32 * st;
@@ -210,12 +212,17 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const auto rk = span_rsrc(p.k, t0 + 16 * h, live);
-        b.k[h][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0));
-        b.k[h][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64, 0, 0));
+#pragma unroll
+        for (int j = 0; j < KP; ++j)
+          b.k[h][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * j, 0, 0));
         const auto rv = span_rsrc(p.v, t0 + 16 * h, live);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b.v[4 * h + j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + j * ROW, 0, 0));
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (D == 128)
+            b.v[4 * h + j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + j * ROW, 0, 0));
+          else
+            b.v[4 * h + j] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(rv, voff + j * ROW, 0, 0), 0u);
+        }
       }
     } else {
       // two blocks per span: per-lane addresses; a step past the last
@@ -223,13 +230,20 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const char* r = row_ptr(p.k, t0 + 16 * h, m16);
-        b.k[h][0] = *reinterpret_cast<const uint4*>(r + 16 * q4);
-        b.k[h][1] = *reinterpret_cast<const uint4*>(r + 64 + 16 * q4);
+#pragma unroll
+        for (int j = 0; j < KP; ++j) b.k[h][j] = *reinterpret_cast<const uint4*>(r + 64 * j + 16 * q4);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        b.v[j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0, 4 * q4 + j) + 8 * m16);
-        b.v[4 + j] = *reinterpret_cast<const uint2*>(row_ptr(p.v, t0 + 16, 4 * q4 + j) + 8 * m16);
+        const char* r0 = row_ptr(p.v, t0, 4 * q4 + j) + NN * m16;
+        const char* r1 = row_ptr(p.v, t0 + 16, 4 * q4 + j) + NN * m16;
+        if constexpr (D == 128) {
+          b.v[j] = *reinterpret_cast<const uint2*>(r0);
+          b.v[4 + j] = *reinterpret_cast<const uint2*>(r1);
+        } else {
+          b.v[j] = make_uint2(*reinterpret_cast<const uint32_t*>(r0), 0u);
+          b.v[4 + j] = make_uint2(*reinterpret_cast<const uint32_t*>(r1), 0u);
+        }
       }
     }
   };
@@ -257,7 +271,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Fp8Rows& b, int st, auto masked_tag) {
+  auto compute = [&](const Fp8Rows<D>& b, int st, auto masked_tag) {
     constexpr bool masked = decltype(masked_tag)::value;  // the step runs past tok1
     const int t0 = tok0 + 32 * st;
     f32x4_t sacc[2];
@@ -309,8 +323,8 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
       if (masked && t0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + e - 4) >= tok1) vr[e] = make_uint2(0u, 0u);
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4_t va[4];  // columns 8 m16 + 4 half + n, n < 4
+    for (int half = 0; half < NN / 4; ++half) {
+      u32x4_t va[4];  // columns NN m16 + 4 half + n, n < 4
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t a = half ? vr[2 * i].y : vr[2 * i].x;
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
       }
     }
   };
-  auto step = [&](const Fp8Rows& b, int st) {
+  auto step = [&](const Fp8Rows<D>& b, int st) {
     if (st == nsteps - 1) compute(b, st, std::true_type{});
     else compute(b, st, std::false_type{});
   };
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
   // the prologue and the loop, so the waits before a buffer is used count
   // only its own loads (loads issued in another order on one path would make
   // the compiler drain everything at the loop head).
-  Fp8Rows bufA, bufB;
+  Fp8Rows<D> bufA, bufB;
   load(bufA, 0);
   __builtin_amdgcn_sched_barrier(0);
   load(bufB, 1);
@@ -353,70 +367,70 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Lane (m16, q4) holds head m16's columns 32 q4 + 8 i + nn in o[nn][i].
+  // Lane (m16, q4) holds head m16's columns NN (4 q4 + i) + nn in o[nn][i]:
+  // NN consecutive values per i.
   const float l = fp8_sum_xor32(fp8_sum_xor16(run_l));
   if (m16 >= G) return;
   const int64_t row = head0 + m16;
   const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
-  if (nparts_seq == 1) {
-    const float inv = p.v_scale / l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t d0 = row * D + 32 * q4 + 8 * i;
-      float y[8];
-#pragma unroll
-      for (int nn = 0; nn < NN; ++nn) y[nn] = o[nn][i] * inv;
-      if (p.out_f32) {
-        float* of = reinterpret_cast<float*>(p.out) + d0;
-        *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
-        *reinterpret_cast<float4*>(of + 4) = make_float4(y[4], y[5], y[6], y[7]);
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = uint32_t(narrow(T{}, y[2 * k])) | (uint32_t(narrow(T{}, y[2 * k + 1])) << 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + d0) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-    return;
-  }
-  const int64_t prow = row * p.num_parts + part;
+  const bool whole = nparts_seq == 1;
+  const float f = whole ? p.v_scale / l : p.v_scale;
+  const int64_t orow = whole ? row : row * p.num_parts + part;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float* of = p.part_o + prow * D + 32 * q4 + 8 * i;
-    *reinterpret_cast<float4*>(of) =
-        make_float4(o[0][i] * p.v_scale, o[1][i] * p.v_scale, o[2][i] * p.v_scale, o[3][i] * p.v_scale);
-    *reinterpret_cast<float4*>(of + 4) =
-        make_float4(o[4][i] * p.v_scale, o[5][i] * p.v_scale, o[6][i] * p.v_scale, o[7][i] * p.v_scale);
+    const int64_t d0 = orow * D + NN * (4 * q4 + i);
+    float y[NN];
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) y[nn] = o[nn][i] * f;
+    if (!whole || p.out_f32) {
+      float* of = (whole ? reinterpret_cast<float*>(p.out) : p.part_o) + d0;
+#pragma unroll
+      for (int k = 0; k < NN; k += 4) *reinterpret_cast<float4*>(of + k) = make_float4(y[k], y[k + 1], y[k + 2], y[k + 3]);
+    } else {
+      uint32_t w[NN / 2];
+#pragma unroll
+      for (int k = 0; k < NN / 2; ++k) w[k] = uint32_t(narrow(T{}, y[2 * k])) | (uint32_t(narrow(T{}, y[2 * k + 1])) << 16);
+      uint16_t* oh = reinterpret_cast<uint16_t*>(p.out) + d0;
+      if constexpr (NN == 8) *reinterpret_cast<uint4*>(oh) = make_uint4(w[0], w[1], w[2], w[3]);
+      else *reinterpret_cast<uint2*>(oh) = make_uint2(w[0], w[1]);
+    }
   }
+  if (whole) return;
+  const int64_t prow = orow;
   if (q4 == 0) {
     p.part_ml[prow * 2 + 0] = run_mc;
     p.part_ml[prow * 2 + 1] = l;
   }
 }
 
-template <class T, int G>
+template <class T, int D, int G>
 void launch_group(const DecodeParams& p, hipStream_t st) {
   const int64_t seqs_padded = (int64_t(p.num_seqs) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
   const dim3 grid(unsigned(int64_t(p.num_parts) * seqs_padded * p.num_kv_heads));
-  if (p.block_size == 8) hipLaunchKernelGGL((decode_fp8_kernel<T, G, true>), grid, dim3(kWave), 0, st, p);
-  else hipLaunchKernelGGL((decode_fp8_kernel<T, G, false>), grid, dim3(kWave), 0, st, p);
+  if (p.block_size == 8) hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, true>), grid, dim3(kWave), 0, st, p);
+  else hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, false>), grid, dim3(kWave), 0, st, p);
 }
 
-template <class T>
+template <class T, int D>
 void launch_g(const DecodeParams& p, int G, hipStream_t st) {
   switch (G) {
-    case 1: launch_group<T, 1>(p, st); break;
-    case 2: launch_group<T, 2>(p, st); break;
-    case 4: launch_group<T, 4>(p, st); break;
-    default: launch_group<T, 8>(p, st); break;
+    case 1: launch_group<T, D, 1>(p, st); break;
+    case 2: launch_group<T, D, 2>(p, st); break;
+    case 4: launch_group<T, D, 4>(p, st); break;
+    default: launch_group<T, D, 8>(p, st); break;
   }
 }
 
 }  // namespace
 
-pa_status launch_decode_fp8_partitions(const DecodeParams& p, pa_dtype q_dtype, int G, hipStream_t st) {
-  if (q_dtype == PA_F16) launch_g<F16>(p, G, st);
-  else launch_g<BF16>(p, G, st);
+pa_status launch_decode_fp8_partitions(const DecodeParams& p, pa_dtype q_dtype, int D, int G, hipStream_t st) {
+  if (q_dtype == PA_F16) {
+    if (D == 64) launch_g<F16, 64>(p, G, st);
+    else launch_g<F16, 128>(p, G, st);
+  } else {
+    if (D == 64) launch_g<BF16, 64>(p, G, st);
+    else launch_g<BF16, 128>(p, G, st);
+  }
   return launch_status("decode E4M3 partition kernel");
 }
 

@@ -76,8 +76,8 @@ __device__ __forceinline__ Unit unit_of(int id, const DecodeParams& p) {
 }
 
 // Launches decode_fp8_kernel over the fixed-partition grid (E4M3 caches,
-// head_dim 128, q of type q_dtype, G query heads per KV head); the caller
-// launches the combine kernel when contexts span several partitions.
-pa_status launch_decode_fp8_partitions(const DecodeParams& p, pa_dtype q_dtype, int G, hipStream_t st);
+// head_dim D of 64 or 128, q of type q_dtype, G query heads per KV head); the
+// caller launches the combine kernel when contexts span several partitions.
+pa_status launch_decode_fp8_partitions(const DecodeParams& p, pa_dtype q_dtype, int D, int G, hipStream_t st);
 
 }  // namespace pkv
