@@ -307,7 +307,7 @@ def bench_prefix(dev, with_cpu, rounds=200, reps=20):
         def call():
             P.pa_prefill(out, q, kc, vc, t_tab, t_ctx, qs, scale, chunk, stream=stream)
 
-        for _ in range(3):
+        for _ in range(100):    # untimed: lets the matrix-core clock settle (~30-60 ms)
             call()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -677,6 +677,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="leave the prefill, prefix-cache, swap and fp8 objects out")
     ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=200,
+                    help="untimed pa_prefill launches before the timed ones (~60 ms: the matrix-core "
+                         "clock takes that long to settle; 10 launches read ~15%% slow)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--compare-contiguous", action="store_true",
@@ -709,7 +712,7 @@ def main():
         print(json.dumps(res), flush=True)
         return
     if args.mode == "prefill":
-        res = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
+        res = bench_prefill(args.prefill_steps, args.prefill_warmup, dev, not args.no_cpu_baseline)
         if args.copy_calibration:
             copy_calibration(dev)
         res.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
@@ -818,7 +821,7 @@ def main():
     if comparison is not None:
         result["paged_vs_contiguous"] = comparison
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(args.prefill_steps, args.warmup, dev, not args.no_cpu_baseline)
+        result["prefill"] = bench_prefill(args.prefill_steps, args.prefill_warmup, dev, not args.no_cpu_baseline)
         result["prefix_cache"] = bench_prefix(dev, not args.no_cpu_baseline)
         result["swap"] = bench_swap(dev, not args.no_cpu_baseline)
         result["fp8"] = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas,
