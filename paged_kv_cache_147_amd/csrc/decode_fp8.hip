@@ -11,9 +11,11 @@
 // decode_kernel, with both contractions on the matrix cores.  Every E4M3
 // value is exactly a float16 and a bfloat16 value, so codes are widened to
 // q's 16-bit type without rounding; the only roundings are the float32
-// accumulation's and the probabilities' 16-bit split.  head_dim 128.
+// accumulation's and the probabilities' 16-bit split.
 //
-// Per 32-token step, lane (m16 = lane % 16, q4 = lane / 16):
+// Per 32-token step, lane (m16 = lane % 16, q4 = lane / 16), written for
+// head_dim 128 (at 64: two score steps, one 16-byte K piece, 4 V bytes per
+// row and 4 output blocks):
 //   * S^T = K Q^T per 16-token tile (v_mfma_f32_16x16x32): A = the tile's K
 //     rows, lane m16 holding row m16, bytes 16 q4 .. +15 and 64 + 16 q4 ..
 //     +15 (MFMA step kk takes bytes 64 (kk / 2) + 16 q4 + 8 (kk % 2) .. +7;
@@ -31,11 +33,12 @@
 //     rows and regroups bytes into token pairs in registers, so output block
 //     nn of O^T is head_dim column 8 m16 + nn.  P enters as a 16-bit high
 //     part plus the 16-bit rounding of its remainder (two MFMAs).
-// Rows are read with global loads from a scalar base per 16-token span and a
-// fixed per-lane offset; two steps of loads are in flight (register double
-// buffering).  Rows past the partition's end are read from the last block
-// (always inside the pool): their scores are masked and their V codes zeroed,
-// so a stale NaN code there cannot reach the sums.
+// Rows are read with buffer loads from a scalar resource per 16-token span and
+// a fixed per-lane offset (global loads with per-lane addresses when 8-token
+// blocks put two blocks in a span); two steps of loads are in flight
+// (register double buffering).  Rows past the partition's end are read from
+// the last block (always inside the pool): their scores are masked and their
+// V codes zeroed, so a stale NaN code there cannot reach the sums.
 #include "decode_params.h"
 #include "device_common.h"
 
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
     }
   };
   // Blocks of >= 16 tokens: a span is 16 consecutive rows of one block, read
-  // as buffer loads from a scalar resource over those 2 KB plus a fixed lane
+  // as buffer loads from a scalar resource over those 16 rows plus a fixed lane
   // offset and an immediate (no per-lane address arithmetic).
   const uint32_t koff = uint32_t(m16) * ROW + 16u * q4;          // K: row m16, bytes 16 q4 (+64)
   const uint32_t voff = uint32_t(4 * q4) * ROW + uint32_t(NN) * m16;  // V: row 4 q4 (+j), bytes NN m16
