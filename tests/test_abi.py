@@ -205,3 +205,60 @@ def test_prefill_rejects_before_launch():
         setattr(a, field, good)
     a.num_seqs = 0
     assert lib.pa_prefill(ctypes.byref(a), None) == 0                      # nothing to do
+
+
+# ---- E4M3 caches: host-side validation (no GPU needed) ------------------------------
+
+def _fp8(**kw):
+    base = dict(kv_dtype=L.PA_FP8_E4M3, q_dtype=L.PA_BF16, k_scale=0.02, v_scale=0.03)
+    base.update(kw)
+    return _args(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_dtype=L.PA_F32), L.PA_E_UNSUPPORTED),          # queries must be 16-bit
+    (dict(q_dtype=9), L.PA_E_UNSUPPORTED),
+    (dict(out_dtype=L.PA_F16), L.PA_E_UNSUPPORTED),        # 16-bit output must be q's type
+    (dict(partition_size=-1), L.PA_E_UNSUPPORTED),         # no balanced schedule over codes
+    (dict(k_scale=0.0), L.PA_E_INVAL),
+    (dict(v_scale=-1.0), L.PA_E_INVAL),
+    (dict(k_scale=float("nan")), L.PA_E_INVAL),
+    (dict(v_scale=float("inf")), L.PA_E_INVAL),
+    (dict(head_dim=96), L.PA_E_UNSUPPORTED),
+])
+def test_fp8_decode_rejects_before_launch(kw, code):
+    lib = P.raw()
+    a = _fp8(**kw)
+    n = ctypes.c_size_t()
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == code
+    assert lib.pa_decode(ctypes.byref(a), None) == code
+    assert lib.pa_last_error()
+
+
+def test_fp8_decode_workspace_matches_the_16bit_path():
+    # the E4M3 kernel writes the same (max, sum, weighted sum) records
+    lib = P.raw()
+    n8, n16 = ctypes.c_size_t(), ctypes.c_size_t()
+    for part in (0, 128, 256):
+        assert lib.pa_decode_workspace_bytes(ctypes.byref(_fp8(partition_size=part)), ctypes.byref(n8)) == 0
+        assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(partition_size=part)), ctypes.byref(n16)) == 0
+        assert n8.value == n16.value
+    assert lib.pa_decode(ctypes.byref(_fp8(num_seqs=0)), None) == 0
+
+
+@pytest.mark.parametrize("src,ks,vs,code", [
+    (L.PA_FP8_E4M3, 1.0, 1.0, L.PA_E_UNSUPPORTED),   # the source must be a value type
+    (L.PA_BF16, 0.0, 1.0, L.PA_E_INVAL),
+    (L.PA_BF16, 1.0, float("nan"), L.PA_E_INVAL),
+    (L.PA_F16, float("inf"), 1.0, L.PA_E_INVAL),
+])
+def test_write_kv_fp8_rejects_before_launch(src, ks, vs, code):
+    lib = P.raw()
+    assert lib.pa_write_kv_fp8(1, 1, 1, 1, src, 1, 4, 8, 128, 16, 64, ks, vs, None) == code
+
+
+def test_bit_copies_accept_e4m3_caches():
+    lib = P.raw()
+    assert lib.pa_write_kv(None, None, None, None, None, 0, 8, 128, 16, 64, L.PA_FP8_E4M3, None) == 0
+    assert lib.pa_copy_blocks(None, None, None, 0, 8, 64, 16, 64, L.PA_FP8_E4M3, None) == 0
+    assert lib.pa_write_kv_fp8(None, None, None, None, L.PA_F32, None, 0, 8, 64, 8, 64, 0.5, 0.5, None) == 0
