@@ -284,3 +284,66 @@ def test_full_size_gqa_sampled(share):
     idx = tuple(np.array(pairs).T)
     assert_close(got[idx], ref[idx], wl.dtype, wl.name + " E4M3")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_decode_edge_contexts(B):
+    # 1, 7, 8, 9 tokens; a step boundary (32, 33); exactly one and two 512-token
+    # partitions and one past; the table's maximum
+    ctx = [1, 7, 8, 9, 32, 33, 512, 513, 1024, 1025, 2048]
+    wl = W.independent(f"fp8_edge_{B}", ctx, (8, 2, 128, B, "bf16"), num_blocks=2 * 2048 // B * 6,
+                       max_blocks=2048 // B, seed=B)
+    print(f"[fp8 decode] edge contexts B={B}", flush=True)
+    case = Fp8Case(wl)
+    ref = case.oracle()
+    for part in (0, 512, 64):
+        assert_close(case.decode(partition_size=part).cpu().numpy(), ref, "bf16", f"edge B={B} partition {part}")
+    # one token: the output is that token's dequantised V row, exactly
+    one = case.decode().cpu().numpy()[0]
+    blk, row = case.tables[0][0], 0
+    vrow = (F.VALUES[case.vc[blk, :, row, :]] * np.float32(case.v_scale)).astype(np.float32)
+    assert np.array_equal(one.reshape(2, 4, 128)[:, 0, :], vrow.astype(np.float32))
+
+
+def _codes_case(name, kfill, vfill, k_scale, v_scale, ctx=(5, 77, 600)):
+    """A batch whose caches hold given codes everywhere (oracle-side arrays)."""
+    wl = W.independent(name, list(ctx), (8, 2, 128, 16, "bf16"), num_blocks=120, max_blocks=40, seed=7)
+    case = Fp8Case(wl, k_scale, v_scale)
+    case.kc = kfill(case.kc.copy())
+    case.vc = vfill(case.vc.copy())
+    case.dev["k"] = torch.from_numpy(case.kc).cuda()
+    case.dev["v"] = torch.from_numpy(case.vc).cuda()
+    return case
+
+
+def test_decode_degenerate_caches():
+    rng = np.random.default_rng(3)
+    # all-zero keys: every score 0, the output is the mean of the V rows
+    case = _codes_case("fp8_zero_k", lambda k: np.zeros_like(k), lambda v: v, 1.0, 0.05)
+    got = case.decode().cpu().numpy()
+    assert_close(got, case.oracle(), "bf16", "zero keys")
+    # saturated codes (+-448) under large scales: scores far beyond the exponent
+    # range of float32 exponentials before the max is taken out
+    sat = lambda a: np.where(rng.random(a.shape) < 0.5, 0x7E, 0xFE).astype(np.uint8)
+    case = _codes_case("fp8_sat", sat, sat, 4.0, 2.0)
+    got = case.decode().cpu().numpy()
+    ref = case.oracle()
+    assert np.isfinite(got).all()
+    assert_close(got / 896.0, ref / 896.0, "bf16", "saturated codes (outputs in units of 448 * v_scale)")
+    # subnormal codes only (values m/8 * 2^-6)
+    sub = lambda a: (rng.integers(0, 8, size=a.shape) | (rng.integers(0, 2, size=a.shape) << 7)).astype(np.uint8)
+    case = _codes_case("fp8_sub", sub, sub, 1.0, 1.0)
+    assert_close(case.decode().cpu().numpy(), case.oracle(), "bf16", "subnormal codes")
+
+
+def test_decode_nan_code_in_context_poisons_only_its_sequence():
+    case = _codes_case("fp8_nan", lambda k: k, lambda v: v, 1 / 56, 1 / 72)
+    blk = case.tables[1][0]
+    case.kc[blk, 0, 3, 17] = 0x7F                  # a NaN key code in sequence 1, KV head 0
+    case.dev["k"] = torch.from_numpy(case.kc).cuda()
+    got = case.decode().cpu().numpy()
+    ref = case.oracle()
+    assert np.isnan(ref[1, :4]).all() and np.isnan(got[1, :4]).all()   # the group of KV head 0
+    keep = np.ones(got.shape[:2], dtype=bool)
+    keep[1, :4] = False
+    assert_close(got[keep], ref[keep], "bf16", "other rows")
