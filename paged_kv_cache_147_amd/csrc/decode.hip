@@ -216,11 +216,19 @@ constexpr int kMaxWaves = 8192;       // pieces the workspace is sized for, at m
 // q.K on the matrix cores: for a GQA group (G >= 2) of 16-bit heads, the
 // scores of 16 tokens x G heads are a small dense contraction over head_dim,
 // done as head_dim / 32 v_mfma_f32_16x16x32 steps (A = 16 K rows, B = the
-// group's queries padded to 16 columns).  A 16-token tile must sit inside one
-// block (block_size >= 16, or the contiguous layout).  MHA (G == 1), float32
-// caches and 8-token blocks use packed dot products on the vector ALUs.
+// group's queries padded to 16 columns).  MHA (G == 1) and float32 caches use
+// packed dot products on the vector ALUs.
 template <class T, int G>
 constexpr bool mfma_capable() { return T::bytes == 2 && G >= 2; }
+
+// Score path of a decode_kernel instance.  kScoresMfma reads a 16-token tile
+// as 16 consecutive rows of one block (block_size >= 16, or the contiguous
+// layout) through one scalar resource; kScoresMfmaSplit serves 8-token blocks,
+// where the tile's two halves lie in two blocks and each half of the lanes
+// addresses its own.
+constexpr int kScoresValu = 0;
+constexpr int kScoresMfma = 1;
+constexpr int kScoresMfmaSplit = 2;
 
 // Passes (of 8 token rows) held by one V load buffer; two buffers alternate,
 // so up to 2 * passes_per_buffer * 8 rows are in flight per wave.  The
@@ -300,7 +308,7 @@ __device__ __forceinline__ int piece_of_workgroup(int id, const Sched& sc) {
 
 // 16-bit caches with G <= 4 fit 128 registers, i.e. 4 waves per SIMD (the
 // balanced schedule's loops need the hint to get there without spilling).
-template <class T, int D, int G, bool PAGED, bool MFMA, bool BAL>
+template <class T, int D, int G, bool PAGED, int MFMA, bool BAL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(T::bytes == 2 && G <= 4 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
   constexpr int EPC = 16 / T::bytes;          // elements per 16-byte chunk
@@ -308,6 +316,7 @@ void decode_kernel(DecodeParams p) {
   constexpr int NCH = ROW_BYTES / 128;        // chunks per lane per row
   constexpr int NV = NCH * EPC;               // values per lane per row (= D / 8)
   static_assert(!MFMA || mfma_capable<T, G>(), "MFMA scores need 16-bit data and G >= 2");
+  static_assert(MFMA != kScoresMfmaSplit || PAGED, "split tiles serve 8-token blocks");
   constexpr int U = MFMA ? 2 : passes_per_buffer<G>();
   constexpr int KT = 1;  // 16-token score tiles per K buffer (MFMA path)
   constexpr int KK = D / 32;                  // MFMA steps over head_dim
@@ -464,12 +473,23 @@ void decode_kernel(DecodeParams p) {
       auto load_tile = [&](uint4 (&kt)[KK], int tile) {
         int live0, live1;
         const char* rows0 = pass_rows(p.k, 2 * tile, live0);
-        pass_rows(p.k, 2 * tile + 1, live1);
-        const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
-        const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
-        const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
+        const char* rows1 = pass_rows(p.k, 2 * tile + 1, live1);
+        if constexpr (MFMA == kScoresMfmaSplit) {
+          // 8-token blocks: lanes m < 8 read the first pass's block, lanes
+          // m >= 8 the second's (a past-the-end pass is the last one again,
+          // its scores masked), each from its own 64-bit address
+          const bool upper = m >= kRowsPerPass;
+          const int row = min(m & (kRowsPerPass - 1), (upper ? live1 : live0) - 1);
+          const char* rp = (upper ? rows1 : rows0) + row * ROW_BYTES + q4 * 16;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
+          for (int kk = 0; kk < KK; ++kk) kt[kk] = *reinterpret_cast<const uint4*>(rp + kk * 64);
+        } else {
+          const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
+          const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
+          const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
+        }
       };
       float* sink = lds + lds_rows(p.part_tokens) * G + lane;
       auto score_tile = [&](const uint4 (&kt)[KK], int tile) {
@@ -1039,7 +1059,7 @@ void bind_workspace(const Plan& plan, void* ws, DecodeParams* p) {
   p->start_seq = reinterpret_cast<int32_t*>(base + plan.start_off);
 }
 
-template <class T, int D, int G, bool PAGED, bool MFMA>
+template <class T, int D, int G, bool PAGED, int MFMA>
 int occupancy(size_t lds) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, D, G, PAGED, MFMA, true>, kWave, lds) !=
@@ -1068,9 +1088,10 @@ int balanced_waves() {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
   const size_t lds = size_t(lds_floats_balanced<G, D>()) * sizeof(float);
-  int occ = std::min(occupancy<T, D, G, true, false>(lds), occupancy<T, D, G, false, false>(lds));
+  int occ = std::min(occupancy<T, D, G, true, kScoresValu>(lds), occupancy<T, D, G, false, kScoresValu>(lds));
   if constexpr (mfma_capable<T, G>())
-    occ = std::min(occ, std::min(occupancy<T, D, G, true, true>(lds), occupancy<T, D, G, false, true>(lds)));
+    occ = std::min({occ, occupancy<T, D, G, true, kScoresMfma>(lds), occupancy<T, D, G, false, kScoresMfma>(lds),
+                    occupancy<T, D, G, true, kScoresMfmaSplit>(lds)});
   if (occ <= 0) return 0;
   const int waves = std::max(8, std::min(kMaxWaves, cus * occ) / 8 * 8);
   cache[dev] = waves;
@@ -1081,12 +1102,16 @@ template <class T, int D, int G, bool PAGED, bool BAL>
 void launch_decode(const DecodeParams& p, dim3 grid, hipStream_t st) {
   const size_t lds = size_t(BAL ? lds_floats_balanced<G, D>() : lds_floats<G>(p.part_tokens)) * sizeof(float);
   if constexpr (mfma_capable<T, G>()) {
-    if (!PAGED || p.block_size >= 16) {
-      hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, true, BAL>), grid, dim3(kWave), lds, st, p);
-      return;
+    if constexpr (PAGED) {
+      if (p.block_size < 16) {
+        hipLaunchKernelGGL((decode_kernel<T, D, G, true, kScoresMfmaSplit, BAL>), grid, dim3(kWave), lds, st, p);
+        return;
+      }
     }
+    hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, kScoresMfma, BAL>), grid, dim3(kWave), lds, st, p);
+    return;
   }
-  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, false, BAL>), grid, dim3(kWave), lds, st, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, kScoresValu, BAL>), grid, dim3(kWave), lds, st, p);
 }
 
 template <class T, int D, int G, bool PAGED>
