@@ -831,8 +831,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams 
 // (64 records per round), so the max and the sum are wave reductions; each
 // lane then owns D / 64 output elements and adds the records in token order,
 // so the result never depends on the order in which the records were written.
-// Every load address is known up front, so the loads of a round are all in
-// flight together.
+// Every load address is known up front: with at most 64 records (the usual
+// case) the (m, l) loads and the first 8 records' outputs are in flight
+// together, so the merge waits on memory about once after the context length.
 //   fixed partitions: record i = partition i, rows (head * num_parts + i);
 //   balanced: the pieces k_lo..k_hi that cut the range, row (slot * G + h)
 //   with slot 2 k_lo + (range starts inside piece k_lo), then 2 k; a range
@@ -881,38 +882,73 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml);
   const float* po = p.part_o + lane * PER;
 
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[rec(i)].x);
+  // Outputs are read kBatch records at a time, all loads of a batch issued
+  // before any is used (an index past the round's last record re-reads that
+  // record, and its term is skipped), so a batch costs one memory round trip;
+  // records are added in token order.
+  constexpr int kBatch = 8;
+  float x[kBatch][PER];
+  auto load_batch = [&](int base, int i0, int n) {
 #pragma unroll
-  for (int mm = 1; mm < kWave; mm <<= 1) M = fmaxf(M, __shfl_xor(M, mm));
-
-  float L = 0.f;
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t r = rec(base + min(i0 + u, n - 1));
+#pragma unroll
+      for (int k = 0; k < PER; ++k) x[u][k] = po[r * D + k];
+    }
+  };
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int base = 0; base < np; base += kWave) {
-    const int n = min(np - base, kWave);
-    const float2 mine = lane < n ? ml[rec(base + lane)] : make_float2(-INFINITY, 0.f);
-    const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past n
-    L += mine.y * f;
-    int i = 0;
-    for (; i + 8 <= n; i += 8) {
-      float x[8][PER];
+  // f: lane i holds the weight of the round's record i.  Terms past the
+  // round's end are computed and dropped by a select (a branch would let the
+  // compiler sink their loads behind it, one round trip each).
+  auto add_batch = [&](int i0, int n, float f) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kBatch; ++u) {
+      const bool live = i0 + u < n;
+      const float fu = __shfl(f, min(i0 + u, kWave - 1));
 #pragma unroll
-        for (int k = 0; k < PER; ++k) x[u][k] = po[rec(base + i + u) * D + k];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float fu = __shfl(f, i + u);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, x[u][k], o[k]);
+      for (int k = 0; k < PER; ++k) {
+        const float y = fmaf(fu, x[u][k], o[k]);
+        o[k] = live ? y : o[k];
       }
     }
-    for (; i < n; ++i) {
-      const float fu = __shfl(f, i);
+  };
+  auto wave_max = [](float v) {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(fu, po[rec(base + i) * D + k], o[k]);
+    for (int mm = 1; mm < kWave; mm <<= 1) v = fmaxf(v, __shfl_xor(v, mm));
+    return v;
+  };
+
+  float L = 0.f;
+  if (np <= kWave) {
+    // One round: lane i holds record i's (m, l).  Its load and the first
+    // batch's output loads go out together, ahead of the reductions.
+    const float2 mine = lane < np ? ml[rec(lane)] : make_float2(-INFINITY, 0.f);
+    load_batch(0, 0, np);
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+    const float M = wave_max(mine.x);
+    const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past np
+    L = mine.y * f;
+    add_batch(0, np, f);
+    for (int i0 = kBatch; i0 < np; i0 += kBatch) {
+      load_batch(0, i0, np);
+      add_batch(i0, np, f);
+    }
+  } else {
+    // Rounds of 64 records against the maximum over all of them.
+    float M = -INFINITY;
+    for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[rec(i)].x);
+    M = wave_max(M);
+    for (int base = 0; base < np; base += kWave) {
+      const int n = min(np - base, kWave);
+      const float2 mine = lane < n ? ml[rec(base + lane)] : make_float2(-INFINITY, 0.f);
+      const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past n
+      L += mine.y * f;
+      for (int i0 = 0; i0 < n; i0 += kBatch) {
+        load_batch(base, i0, n);
+        add_batch(i0, n, f);
+      }
     }
   }
 #pragma unroll
