@@ -110,6 +110,24 @@ def measured_traffic(workload):
     return float(m.group(2))
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"cpu_model": model, "cores_available": avail}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The float64 oracle, as it stands, on the first sequences of the batch
     until ~budget_s of work; scaled to GB/s of logical KV."""
@@ -135,7 +153,7 @@ def cpu_baseline(wl, budget_s=10.0):
             "kind": "oracle",
             "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB logical KV), "
                       f"{wall:.1f} s wall, float64 numpy",
-            "seqs_per_s": round(done / wall, 2)}
+            "seqs_per_s": round(done / wall, 2), **host_cpu()}
 
 
 def prefill_flops(ctx, q_start, head_dim, num_q_heads):
@@ -175,7 +193,7 @@ def prefill_cpu_baseline(wl, budget_s=10.0):
     return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, round(cpu / wall)),
             "kind": "oracle",
             "sample": f"first {done} of {wl.num_seqs} sequences, every chunk row and head "
-                      f"({flops / 1e9:.2f} GFLOP), {wall:.1f} s wall, float64 numpy"}
+                      f"({flops / 1e9:.2f} GFLOP), {wall:.1f} s wall, float64 numpy", **host_cpu()}
 
 
 def bench_prefill(steps, warmup, dev, with_cpu):
@@ -488,7 +506,7 @@ def fp8_cpu_baseline(wl, k_scale, v_scale, budget_s=10.0):
             "kind": "oracle",
             "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB of codes), "
                       f"{wall:.1f} s wall, float64 numpy",
-            "seqs_per_s": round(done / wall, 2)}
+            "seqs_per_s": round(done / wall, 2), **host_cpu()}
 
 
 def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, with_cpu, bf16_decode_ms=None,
