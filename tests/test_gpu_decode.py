@@ -119,12 +119,12 @@ def test_contiguous_kernel_matches_oracle_and_paged_bitwise():
         out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), device="cuda")
         P.pa_decode_contiguous(out, dev.q, kd, vd, torch.from_numpy(ctx).cuda(), wl.scale)
         paged = dev.decode()
-        if B >= 16:
-            # same score path (matrix cores), same order of every sum: bit-identical
-            assert torch.equal(out, paged), B
-            bal = torch.empty_like(out)
-            P.pa_decode_contiguous(bal, dev.q, kd, vd, torch.from_numpy(ctx).cuda(), wl.scale, partition_size=-1)
-            assert torch.equal(bal, dev.decode(partition_size=-1)), B      # balanced cuts agree too
+        # same score path (matrix cores; at B = 8 a tile's halves come from two
+        # blocks), same order of every sum: bit-identical
+        assert torch.equal(out, paged), B
+        bal = torch.empty_like(out)
+        P.pa_decode_contiguous(bal, dev.q, kd, vd, torch.from_numpy(ctx).cuda(), wl.scale, partition_size=-1)
+        assert torch.equal(bal, dev.decode(partition_size=-1)), B      # balanced cuts agree too
         ref = A.contiguous_decode(wl.q, k, v, ctx, wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads)
         assert_close(out.cpu().numpy(), ref, wl.dtype, f"contiguous B={B}")
         assert_close(paged.cpu().numpy(), ref, wl.dtype, f"paged B={B}")
@@ -141,6 +141,18 @@ def test_contiguous_odd_partitions(part):
     P.pa_decode_contiguous(out, q, kd, vd, torch.from_numpy(ctx).cuda(), wl.scale, partition_size=part)
     ref = A.contiguous_decode(wl.q, k, v, ctx, wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads)
     assert_close(out.cpu().numpy(), ref, wl.dtype, f"contiguous partition {part}")
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 1)])
+def test_more_than_64_partition_records(dtype, G):
+    # 8-token partitions: up to 138 records per (sequence, head), so the merge
+    # runs several rounds of 64 records and several batches in each
+    ctx = [1, 9, 64, 520, 1100]
+    wl = W.independent(f"many_{dtype}", ctx, (2 * G, 2, 64, 8, dtype), 512, 140, seed=17)
+    dev = NativeDeviceRun(wl)
+    ref = oracle_out(wl)
+    for part in (8, 16):
+        assert_close(dev.decode(partition_size=part).cpu().numpy(), ref, dtype, f"{wl.name} partition {part}")
 
 
 def test_edge_contexts():
