@@ -19,9 +19,10 @@
 //   * the workgroup walks the keys its rows can see in steps of 32.  Each
 //     step's K and V rows are gathered through the block table straight into
 //     LDS by global_load_lds_dwordx4 (16 bytes per lane, no registers on the
-//     way), into a ring of 4 stages, so three steps of loads are in flight
-//     while one is computed; the block ids come from scalar loads, which keeps
-//     the vector-memory counter for the ring alone;
+//     way), into a ring of 4 stages used two steps at a time: while a pair
+//     of steps is computed the next pair's loads are in flight, and the
+//     waves meet once per pair; the block ids come from scalar loads, which
+//     keeps the vector-memory counter for the ring alone;
 //   * rows sit in LDS unpadded, their 16-byte chunks permuted by an XOR of
 //     the row index, so the K reads and the transposing V reads below spread
 //     over the banks;
@@ -195,11 +196,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int ROW = D * 2;              // bytes per staged row
   constexpr int TILE = kKeys * ROW;       // bytes of one step's K (or V) rows
   constexpr int NDMA = TILE / (kThreads * 16);   // 16-byte pieces per thread per tile
-  constexpr int NL = 2 * NDMA;            // ring loads per lane per step (K and V)
   constexpr int TPW = kRows / G;          // chunk tokens per wave
   constexpr int TPB = TPW * kWaves;       // chunk tokens per workgroup
   static_assert(TILE % (kThreads * 16) == 0, "a step's tile must split into whole wave loads");
-  static_assert((kStages - 2) * NL < 64, "vmcnt holds at most 63");
+  static_assert(kStages == 4, "steps go in pairs: two stages computed while two fill");
 
   __shared__ __align__(16) char lds[kStages][2][TILE];   // [stage][K, V][32 rows]
 
@@ -311,9 +311,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int last_row = (ctx - 1) & bmask;
   const int64_t head_off = int64_t(g) * p.tile_bytes;
   const int64_t blk_stride = int64_t(p.num_kv_heads) * p.tile_bytes;
-  // The block ids of a step are fetched (scalar loads) one step before its
-  // loads are issued, so their latency hides behind a step of math.
-  int ids[NDMA];
+  // The block ids of a step are fetched (scalar loads) a pair of steps
+  // before its loads are issued, so their latency hides behind the math.
+  // ids[step % 2] holds them.
+  int ids[2][NDMA];
   auto block_index = [&](int step, int c) {
     // a step spans whole blocks (B divides 32); keys past the context
     // re-read rows of the last block (their scores are masked)
@@ -321,13 +322,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   auto fetch = [&](int step) {
 #pragma unroll
-    for (int c = 0; c < NDMA; ++c) ids[c] = table[block_index(step, c)];
+    for (int c = 0; c < NDMA; ++c) ids[step & 1][c] = table[block_index(step, c)];
   };
   auto issue = [&](int step) {            // ids hold this step's block ids
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       const int bidx = block_index(step, c);
-      const int blk = min(max(ids[c], 0), p.num_blocks - 1);
+      const int blk = min(max(ids[step & 1][c], 0), p.num_blocks - 1);
       const int cap = bidx == last_blk ? last_row : bmask;
       const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
       const int64_t at = int64_t(blk) * blk_stride + head_off;
@@ -364,13 +365,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) qb[j][kk] ^= 0x80008000u;
   }
-#pragma unroll
-  for (int st = 1; st < kStages - 1; ++st)
-    if (st < nsteps) {
-      fetch(st);
-      issue(st);
-    }
-  if (kStages - 1 < nsteps) fetch(kStages - 1);
+  if (1 < nsteps) {
+    fetch(1);
+    issue(1);
+  }
+  if (2 < nsteps) fetch(2);
+  if (3 < nsteps) fetch(3);
 
   // LDS read offsets.  K (A operand of S^T): lane (q4, m16) reads key row
   // m16 (+16 for the second tile), chunk 4 kk + q4.  V^T (transposing reads):
@@ -473,21 +473,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // Ring: step st lives in stage st % kStages.  Before computing step st the
-  // wave waits for its own loads of st (the later steps' loads, at most
-  // kStages - 2 of them, stay in flight) and meets the others; the stage it
-  // then refills held step st - 1, which every wave has finished.
-  for (int st = 0; st < nsteps; ++st) {
-    const int ahead = min(kStages - 2, nsteps - 1 - st);   // later steps already issued
-    if (ahead >= 2) wait_and_meet<2 * NL>();
-    else if (ahead == 1) wait_and_meet<NL>();
-    else wait_and_meet<0>();
-    if (st + kStages - 1 < nsteps) issue(st + kStages - 1);
-    if (st * kKeys <= wave_last) {                      // some row of the wave sees this step
-      if (st * kKeys + kKeys - 1 > wave_first) compute(st, std::true_type{});
-      else compute(st, std::false_type{});
+  // Ring: step st lives in stage st % kStages, and steps go in pairs.  Before
+  // computing steps st and st + 1 the wave waits for all its loads (those of
+  // the pair) and meets the others; the two stages it then refills, with
+  // steps st + 2 and st + 3, held the previous pair, which every wave has
+  // finished.  The next pair's loads are in flight while this pair is
+  // computed, and there is one barrier per two steps.
+  for (int st = 0; st < nsteps; st += 2) {
+    wait_and_meet<0>();
+    if (st + 2 < nsteps) issue(st + 2);
+    if (st + 3 < nsteps) issue(st + 3);
+    if (st + 4 < nsteps) fetch(st + 4);
+    if (st + 5 < nsteps) fetch(st + 5);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s2 = st + h;
+      if (s2 < nsteps && s2 * kKeys <= wave_last) {
+        if (s2 * kKeys + kKeys - 1 > wave_first) compute(s2, std::true_type{});
+        else compute(s2, std::false_type{});
+      }
     }
-    if (st + kStages < nsteps) fetch(st + kStages);
   }
 
   // the loop's last wait drained the ring; rows of the wave now end
