@@ -385,9 +385,26 @@ def pa_swap_in(k_cache, v_cache, blocks, host, stream=None):
     _swap(_lib.pa_swap_in, k_cache, v_cache, blocks, host, stream)
 
 
+def _check_shapes(out, q, k, v, d, seqs, block_tables=None, ctx_lens=None):
+    """The C ABI receives pointers and sizes only, so every size it derives
+    from the tensors here must describe them all: a mismatch would send the
+    kernels past the end of a buffer."""
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v caches must have the same shape and dtype")
+    if q.dim() != 3 or q.shape[2] != d:
+        raise ValueError(f"q must be [rows][num_q_heads][{d}]")
+    if out is not None and out.shape != q.shape:
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}")
+    if block_tables is not None and (block_tables.dim() != 2 or block_tables.shape[0] != seqs):
+        raise ValueError(f"block_tables must be [{seqs}][max_blocks]")
+    if ctx_lens is not None and (ctx_lens.dim() != 1 or ctx_lens.shape[0] != seqs):
+        raise ValueError(f"ctx_lens must hold {seqs} entries")
+
+
 def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
                 partition_size=0, workspace=None, k_scale=1.0, v_scale=1.0):
     nb, hkv, B, d = _cache_dims(k_cache)
+    _check_shapes(out, q, k_cache, v_cache, d, q.shape[0], block_tables, ctx_lens)
     S, hq, dq = q.shape
     a = pa_decode_args()
     a.out = out.data_ptr() if out is not None else None
@@ -449,7 +466,12 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0
 
 
 def contig_args(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_size=0, workspace=None):
+    if k.dim() != 4:
+        raise ValueError("k and v must be [num_seqs][num_kv_heads][capacity][head_dim]")
     S, hkv, cap, d = k.shape
+    _check_shapes(out, q, k, v, d, S, None, ctx_lens)
+    if q.shape[0] != S:
+        raise ValueError(f"q must hold {S} sequences, as k and v do")
     a = pa_contig_args()
     a.out = out.data_ptr() if out is not None else None
     a.out_dtype = DTYPE_OF[out.dtype] if out is not None else PA_F32
@@ -511,6 +533,9 @@ def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, s
 
 def prefill_args(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scale, max_chunk):
     nb, hkv, B, d = _cache_dims(k_cache)
+    _check_shapes(out, q, k_cache, v_cache, d, ctx_lens.shape[0], block_tables, ctx_lens)
+    if q_start.dim() != 1 or q_start.shape[0] != ctx_lens.shape[0] + 1:
+        raise ValueError("q_start needs num_seqs + 1 entries")
     T, hq, dq = q.shape
     a = pa_prefill_args()
     a.out = out.data_ptr() if out is not None else None

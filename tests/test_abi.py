@@ -262,3 +262,54 @@ def test_bit_copies_accept_e4m3_caches():
     assert lib.pa_write_kv(None, None, None, None, None, 0, 8, 128, 16, 64, L.PA_FP8_E4M3, None) == 0
     assert lib.pa_copy_blocks(None, None, None, 0, 8, 64, 16, 64, L.PA_FP8_E4M3, None) == 0
     assert lib.pa_write_kv_fp8(None, None, None, None, L.PA_F32, None, 0, 8, 64, 8, 64, 0.5, 0.5, None) == 0
+
+
+def _decode_tensors(S=3, hq=8, hkv=2, d=64, B=16, nb=12, mb=4):
+    import torch
+    bf = torch.bfloat16
+    return dict(out=torch.empty(S, hq, d), q=torch.empty(S, hq, d, dtype=bf),
+                k_cache=torch.empty(nb, hkv, B, d, dtype=bf), v_cache=torch.empty(nb, hkv, B, d, dtype=bf),
+                block_tables=torch.zeros(S, mb, dtype=torch.int32), ctx_lens=torch.ones(S, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("bad", ["v_shape", "v_dtype", "q_dim", "out_shape", "table_rows", "ctx_len"])
+def test_binding_refuses_inconsistent_shapes(bad):
+    # the ABI sees pointers and sizes only; the binding checks that the tensors
+    # agree with the sizes it passes (CPU tensors: argument building only)
+    import torch
+    t = _decode_tensors()
+    L.decode_args(scale=0.1, **t)                       # consistent: accepted
+    if bad == "v_shape":
+        t["v_cache"] = torch.empty(12, 2, 16, 32, dtype=torch.bfloat16)
+    elif bad == "v_dtype":
+        t["v_cache"] = t["v_cache"].half()
+    elif bad == "q_dim":
+        t["q"] = torch.empty(3, 8, 128, dtype=torch.bfloat16)
+    elif bad == "out_shape":
+        t["out"] = torch.empty(3, 4, 64)
+    elif bad == "table_rows":
+        t["block_tables"] = torch.zeros(2, 4, dtype=torch.int32)
+    else:
+        t["ctx_lens"] = torch.ones(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        L.decode_args(scale=0.1, **t)
+
+
+def test_binding_refuses_inconsistent_prefill_and_contiguous_shapes():
+    import torch
+    t = _decode_tensors()
+    qs = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    L.prefill_args(t["out"], t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["ctx_lens"], qs, 0.1, 1)
+    with pytest.raises(ValueError):
+        L.prefill_args(t["out"], t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["ctx_lens"],
+                       qs[:3], 0.1, 1)
+    with pytest.raises(ValueError):
+        L.prefill_args(torch.empty(2, 8, 64), t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                       t["ctx_lens"], qs, 0.1, 1)
+    k = torch.empty(3, 2, 32, 64, dtype=torch.bfloat16)
+    L.contig_args(t["out"], t["q"], k, k.clone(), t["ctx_lens"], 0.1)
+    with pytest.raises(ValueError):
+        L.contig_args(t["out"], t["q"], k, torch.empty(3, 2, 16, 64, dtype=torch.bfloat16), t["ctx_lens"], 0.1)
+    with pytest.raises(ValueError):
+        L.contig_args(t["out"], t["q"], torch.empty(4, 2, 32, 64, dtype=torch.bfloat16),
+                      torch.empty(4, 2, 32, 64, dtype=torch.bfloat16), t["ctx_lens"], 0.1)
