@@ -303,15 +303,19 @@ class BlockPool:
 # Device operations on torch tensors
 # ---------------------------------------------------------------------------
 
-def _cache_dims(k_cache):
+def _cache_dims(k_cache, v_cache=None):
+    """Sizes of a [num_blocks][num_kv_heads][block_size][head_dim] cache pair
+    (the V cache, when given, must match the K cache)."""
     if k_cache.dim() != 4:
         raise ValueError("cache must be [num_blocks][num_kv_heads][block_size][head_dim]")
+    if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
+        raise ValueError("k and v caches must have the same shape and dtype")
     return k_cache.shape
 
 
 def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     """Scatter [T][Hkv][d] rows into the caches at ``slot_mapping`` (int64)."""
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     if slot_mapping.dtype != torch.int64:
         raise ValueError("slot_mapping must be int64")
     T = slot_mapping.numel()
@@ -328,7 +332,7 @@ def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
 def pa_write_kv_fp8(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale, v_scale, stream=None):
     """Quantise [T][Hkv][d] rows (float32 / float16 / bfloat16) to E4M3 codes
     in the caches (uint8 or float8_e4m3fn) at ``slot_mapping`` (int64)."""
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     if DTYPE_OF.get(k_cache.dtype) != PA_FP8_E4M3 or v_cache.dtype != k_cache.dtype:
         raise ValueError("caches must be uint8 or float8_e4m3fn")
     if slot_mapping.dtype != torch.int64:
@@ -349,7 +353,7 @@ def pa_write_kv_fp8(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale, v_sca
 
 def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
     """Copy whole blocks for each (src, dst) row of the int32 ``pairs`` [n][2]."""
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
         raise ValueError("pairs must be int32 [n][2]")
     n = pairs.numel() // 2
@@ -359,7 +363,7 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
 
 
 def _swap(fn, k_cache, v_cache, blocks, host, stream):
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     if blocks.dtype != torch.int32:
         raise ValueError("blocks must be int32")
     _dev(k_cache), _dev(v_cache), _dev(blocks)
@@ -403,7 +407,7 @@ def _check_shapes(out, q, k, v, d, seqs, block_tables=None, ctx_lens=None):
 
 def decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
                 partition_size=0, workspace=None, k_scale=1.0, v_scale=1.0):
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     _check_shapes(out, q, k_cache, v_cache, d, q.shape[0], block_tables, ctx_lens)
     S, hq, dq = q.shape
     a = pa_decode_args()
@@ -532,7 +536,7 @@ def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, s
 
 
 def prefill_args(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scale, max_chunk):
-    nb, hkv, B, d = _cache_dims(k_cache)
+    nb, hkv, B, d = _cache_dims(k_cache, v_cache)
     _check_shapes(out, q, k_cache, v_cache, d, ctx_lens.shape[0], block_tables, ctx_lens)
     if q_start.dim() != 1 or q_start.shape[0] != ctx_lens.shape[0] + 1:
         raise ValueError("q_start needs num_seqs + 1 entries")

@@ -313,3 +313,20 @@ def test_binding_refuses_inconsistent_prefill_and_contiguous_shapes():
     with pytest.raises(ValueError):
         L.contig_args(t["out"], t["q"], torch.empty(4, 2, 32, 64, dtype=torch.bfloat16),
                       torch.empty(4, 2, 32, 64, dtype=torch.bfloat16), t["ctx_lens"], 0.1)
+
+
+def test_cache_ops_refuse_mismatched_v_cache():
+    import torch
+    k = torch.empty(4, 2, 16, 64, dtype=torch.bfloat16)
+    v = torch.empty(4, 2, 8, 64, dtype=torch.bfloat16)
+    rows = torch.empty(1, 2, 64, dtype=torch.bfloat16)
+    slots = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_write_kv(k, v, rows, rows, slots)
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_copy_blocks(k, v, torch.zeros(1, 2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_swap_out(k, v, torch.zeros(1, dtype=torch.int32), torch.empty(1))
+    k8 = torch.empty(4, 2, 16, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_write_kv_fp8(k8, k8[:, :, :8].contiguous(), rows, rows, slots, 1.0, 1.0)
