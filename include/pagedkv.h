@@ -340,7 +340,7 @@ pa_status pa_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_
 typedef struct pa_decode_args {
   void* out;                   /* [S][Hq][head_dim], out_dtype */
   pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
-  const void* q;               /* [S][Hq][head_dim], kv_dtype */
+  const void* q;               /* [S][Hq][head_dim], q_dtype */
   const void* k_cache;         /* layout above, kv_dtype */
   const void* v_cache;
   pa_dtype kv_dtype;
@@ -363,8 +363,11 @@ typedef struct pa_decode_args {
   void* workspace;             /* device scratch, >= pa_decode_workspace_bytes,
                                   256-byte aligned */
   size_t workspace_bytes;
+  pa_dtype q_dtype;            /* q's element type.  f32 / f16 / bf16 caches: must equal
+                                  kv_dtype (PA_E_INVAL otherwise: the kernels read q at the
+                                  cache's element size).  E4M3 caches: PA_F16 or PA_BF16,
+                                  and out_dtype is PA_F32 or q_dtype. */
   /* E4M3 caches (kv_dtype PA_FP8_E4M3) only; ignored otherwise: */
-  pa_dtype q_dtype;            /* PA_F16 or PA_BF16: q's dtype; out_dtype is PA_F32 or q_dtype */
   float k_scale;               /* finite, > 0: K element = value(code) * k_scale */
   float v_scale;               /* finite, > 0 */
 } pa_decode_args;
@@ -433,6 +436,7 @@ typedef struct pa_prefill_args {
   int32_t num_blocks;          /* physical blocks in the caches */
   int32_t max_chunk;           /* >= every n_s; sizes the grid */
   float scale;
+  pa_dtype q_dtype;            /* q's element type: must equal kv_dtype (PA_E_INVAL otherwise) */
 } pa_prefill_args;
 pa_status pa_prefill(const pa_prefill_args* args, pa_stream stream);
 
@@ -477,6 +481,7 @@ typedef struct pa_contig_args {
                                   multiple of 8, at most 512 */
   void* workspace;
   size_t workspace_bytes;
+  pa_dtype q_dtype;            /* q's element type: must equal kv_dtype (PA_E_INVAL otherwise) */
 } pa_contig_args;
 
 pa_status pa_decode_contiguous_workspace_bytes(const pa_contig_args* args, size_t* bytes_out);

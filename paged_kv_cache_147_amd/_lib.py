@@ -74,7 +74,8 @@ class pa_contig_args(ctypes.Structure):
                 ("kv_dtype", c_i32), ("ctx_lens", c_vp), ("num_seqs", c_i32),
                 ("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
                 ("capacity", c_i32), ("max_ctx", c_i32), ("scale", c_f32),
-                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+                ("partition_size", c_i32), ("workspace", c_vp), ("workspace_bytes", c_sz),
+                ("q_dtype", c_i32)]
 
 
 class pa_prefill_args(ctypes.Structure):
@@ -82,7 +83,7 @@ class pa_prefill_args(ctypes.Structure):
                 ("kv_dtype", c_i32), ("block_tables", c_vp), ("ctx_lens", c_vp), ("q_start", c_vp),
                 ("num_seqs", c_i32), ("num_rows", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
                 ("head_dim", c_i32), ("block_size", c_i32), ("max_blocks", c_i32), ("num_blocks", c_i32),
-                ("max_chunk", c_i32), ("scale", c_f32)]
+                ("max_chunk", c_i32), ("scale", c_f32), ("q_dtype", c_i32)]
 
 
 _SIGS = {
@@ -395,6 +396,9 @@ def _check_shapes(out, q, k, v, d, seqs, block_tables=None, ctx_lens=None):
     kernels past the end of a buffer."""
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v caches must have the same shape and dtype")
+    if DTYPE_OF.get(k.dtype) != PA_FP8_E4M3 and q.dtype != k.dtype:
+        # the kernels read q at the cache's element size
+        raise ValueError(f"q must have the cache dtype {k.dtype} (got {q.dtype})")
     if q.dim() != 3 or q.shape[2] != d:
         raise ValueError(f"q must be [rows][num_q_heads][{d}]")
     if out is not None and out.shape != q.shape:
@@ -447,6 +451,16 @@ def workspace_for(nbytes, device):
     return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def _workspace_on(nbytes, device, stream):
+    """A workspace made by torch's caching allocator on the current stream but
+    used on ``stream``: when that is another stream, the allocator is told, so
+    the memory is not handed out again before the work queued there has run."""
+    ws = workspace_for(nbytes, device)
+    if stream is not None and stream.value != torch.cuda.current_stream(device).cuda_stream:
+        ws.record_stream(torch.cuda.ExternalStream(stream.value, device=device))
+    return ws
+
+
 def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
               partition_size=0, workspace=None, stream=None, k_scale=1.0, v_scale=1.0):
     """Paged decode attention into ``out`` ([S][Hq][d], float32 or the cache
@@ -462,7 +476,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0
     if workspace is None:
         need = pa_decode_workspace_bytes(a)
         if need:
-            workspace = workspace_for(need, q.device)
+            workspace = _workspace_on(need, q.device, stream)
             a.workspace = workspace.data_ptr()
             a.workspace_bytes = workspace.numel()
     check(_lib.pa_decode(ctypes.byref(a), stream if stream is not None else current_stream()), "pa_decode")
@@ -484,6 +498,7 @@ def contig_args(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_size=0, work
     a.ctx_lens = ctx_lens.data_ptr() if ctx_lens is not None else None
     a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = q.shape[0], q.shape[1], hkv, d
     a.capacity, a.max_ctx, a.scale, a.partition_size = cap, max_ctx, scale, partition_size
+    a.q_dtype = DTYPE_OF.get(q.dtype, -1)
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -506,7 +521,7 @@ def pa_decode_contiguous(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_siz
     if workspace is None:
         need = pa_decode_contiguous_workspace_bytes(a)
         if need:
-            workspace = workspace_for(need, q.device)
+            workspace = _workspace_on(need, q.device, stream)
             a.workspace = workspace.data_ptr()
             a.workspace_bytes = workspace.numel()
     check(_lib.pa_decode_contiguous(ctypes.byref(a), stream if stream is not None else current_stream()),
@@ -552,6 +567,7 @@ def prefill_args(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, scal
     a.num_q_heads, a.num_kv_heads, a.head_dim = hq, hkv, d
     a.block_size, a.max_blocks, a.num_blocks = B, block_tables.shape[1], nb
     a.max_chunk, a.scale = max_chunk, scale
+    a.q_dtype = DTYPE_OF.get(q.dtype, -1)
     return a
 
 

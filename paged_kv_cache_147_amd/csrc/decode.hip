@@ -1213,6 +1213,9 @@ pa_status check_paged(const pa_decode_args* a, Plan* plan) {
     if (!(a->k_scale > 0.f) || !(a->v_scale > 0.f) || !std::isfinite(a->k_scale) || !std::isfinite(a->v_scale))
       return fail(PA_E_INVAL, "k_scale and v_scale must be finite and positive");
     compute = a->q_dtype;
+  } else if (a->q_dtype != a->kv_dtype) {
+    // the kernels read q at the cache's element size
+    return fail(PA_E_INVAL, "q_dtype must equal kv_dtype for f32, f16 and bf16 caches");
   }
   return plan_decode(a->num_seqs, a->num_q_heads, a->num_kv_heads, a->head_dim, compute,
                      a->out_dtype, a->block_size, bound, a->partition_size, a->scale, plan);
@@ -1225,6 +1228,7 @@ pa_status check_contig(const pa_contig_args* a, Plan* plan) {
     return fail(PA_E_INVAL, "capacity must be a positive multiple of 8");
   if (a->max_ctx < 0 || a->max_ctx > a->capacity)
     return fail(PA_E_INVAL, "max_ctx must be in [0, capacity]");
+  if (a->q_dtype != a->kv_dtype) return fail(PA_E_INVAL, "q_dtype must equal kv_dtype");
   const int bound = a->max_ctx ? a->max_ctx : a->capacity;
   return plan_decode(a->num_seqs, a->num_q_heads, a->num_kv_heads, a->head_dim, a->kv_dtype,
                      a->out_dtype, 0, bound, a->partition_size, a->scale, plan);

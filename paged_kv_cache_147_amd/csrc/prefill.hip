@@ -534,6 +534,7 @@ pa_status check_prefill(const pa_prefill_args* a) {
     return fail(PA_E_UNSUPPORTED, "prefill needs a 16-bit (f16 or bf16) cache");
   if (a->out_dtype != PA_F32 && a->out_dtype != a->kv_dtype)
     return fail(PA_E_UNSUPPORTED, "out dtype must be f32 or the cache dtype");
+  if (a->q_dtype != a->kv_dtype) return fail(PA_E_INVAL, "q_dtype must equal kv_dtype");
   if (a->num_q_heads % a->num_kv_heads) return fail(PA_E_INVAL, "num_q_heads must be a multiple of num_kv_heads");
   const int G = a->num_q_heads / a->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8)

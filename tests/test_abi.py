@@ -62,6 +62,7 @@ def _args(**kw):
                 head_dim=128, block_size=16, max_blocks=64, num_blocks=1024, max_ctx=0,
                 scale=0.088, partition_size=0, workspace=None, workspace_bytes=0)
     base.update(kw)
+    base.setdefault("q_dtype", base["kv_dtype"])
     for k, v in base.items():
         setattr(a, k, v)
     return a
@@ -81,6 +82,9 @@ def _args(**kw):
     (dict(scale=float("inf")), L.PA_E_INVAL),
     (dict(num_seqs=-1), L.PA_E_INVAL),
     (dict(max_blocks=0), L.PA_E_INVAL),
+    (dict(q_dtype=L.PA_F32), L.PA_E_INVAL),          # f32 q with a bf16 cache: would be misread
+    (dict(q_dtype=L.PA_F16), L.PA_E_INVAL),
+    (dict(kv_dtype=L.PA_F32, q_dtype=L.PA_BF16), L.PA_E_INVAL),  # 16-bit q, f32 cache: read past q's end
 ])
 def test_decode_rejects_before_launch(kw, code):
     lib = P.raw()
@@ -132,12 +136,15 @@ def test_contiguous_rejects_before_launch():
     a = L.pa_contig_args()
     for k, v in dict(out=1, out_dtype=0, q=1, k=1, v=1, kv_dtype=2, ctx_lens=1, num_seqs=2,
                      num_q_heads=8, num_kv_heads=8, head_dim=128, capacity=100, max_ctx=0,
-                     scale=0.1, partition_size=0).items():
+                     scale=0.1, partition_size=0, q_dtype=2).items():
         setattr(a, k, v)
     assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_INVAL   # capacity % 8
     a.capacity = 1024
     a.head_dim = 80
     assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED
+    a.head_dim = 128
+    a.q_dtype = L.PA_F32                     # q read at the cache's element size: refused
+    assert lib.pa_decode_contiguous(ctypes.byref(a), None) == L.PA_E_INVAL
 
 
 @pytest.mark.parametrize("S,hkv,max_ctx,expect_parts", [
@@ -191,11 +198,12 @@ def test_prefill_rejects_before_launch():
     a = L.pa_prefill_args()
     for k, v in dict(out=1, out_dtype=L.PA_F32, q=1, k_cache=1, v_cache=1, kv_dtype=L.PA_F32, block_tables=1,
                      ctx_lens=1, q_start=1, num_seqs=2, num_rows=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
-                     block_size=16, max_blocks=8, num_blocks=16, max_chunk=4, scale=0.1).items():
+                     block_size=16, max_blocks=8, num_blocks=16, max_chunk=4, scale=0.1,
+                     q_dtype=L.PA_F32).items():
         setattr(a, k, v)
     assert lib.pa_prefill(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED     # float32 cache
-    a.kv_dtype = L.PA_BF16
-    for field, bad, code in [("head_dim", 96, L.PA_E_UNSUPPORTED), ("num_q_heads", 6, L.PA_E_UNSUPPORTED),
+    a.kv_dtype = a.q_dtype = L.PA_BF16
+    for field, bad, code in [("q_dtype", L.PA_F16, L.PA_E_INVAL), ("q_dtype", L.PA_F32, L.PA_E_INVAL),("head_dim", 96, L.PA_E_UNSUPPORTED), ("num_q_heads", 6, L.PA_E_UNSUPPORTED),
                              ("block_size", 64, L.PA_E_UNSUPPORTED), ("scale", float("inf"), L.PA_E_INVAL),
                              ("max_chunk", -1, L.PA_E_INVAL), ("num_rows", -1, L.PA_E_INVAL),
                              ("out_dtype", L.PA_F16, L.PA_E_UNSUPPORTED)]:
@@ -272,7 +280,7 @@ def _decode_tensors(S=3, hq=8, hkv=2, d=64, B=16, nb=12, mb=4):
                 block_tables=torch.zeros(S, mb, dtype=torch.int32), ctx_lens=torch.ones(S, dtype=torch.int32))
 
 
-@pytest.mark.parametrize("bad", ["v_shape", "v_dtype", "q_dim", "out_shape", "table_rows", "ctx_len"])
+@pytest.mark.parametrize("bad", ["v_shape", "v_dtype", "q_dim", "q_dtype", "out_shape", "table_rows", "ctx_len"])
 def test_binding_refuses_inconsistent_shapes(bad):
     # the ABI sees pointers and sizes only; the binding checks that the tensors
     # agree with the sizes it passes (CPU tensors: argument building only)
@@ -285,6 +293,8 @@ def test_binding_refuses_inconsistent_shapes(bad):
         t["v_cache"] = t["v_cache"].half()
     elif bad == "q_dim":
         t["q"] = torch.empty(3, 8, 128, dtype=torch.bfloat16)
+    elif bad == "q_dtype":
+        t["q"] = torch.empty(3, 8, 64, dtype=torch.float32)
     elif bad == "out_shape":
         t["out"] = torch.empty(3, 4, 64)
     elif bad == "table_rows":
@@ -306,10 +316,15 @@ def test_binding_refuses_inconsistent_prefill_and_contiguous_shapes():
     with pytest.raises(ValueError):
         L.prefill_args(torch.empty(2, 8, 64), t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                        t["ctx_lens"], qs, 0.1, 1)
+    with pytest.raises(ValueError, match="cache dtype"):
+        L.prefill_args(t["out"], t["q"].half(), t["k_cache"], t["v_cache"], t["block_tables"], t["ctx_lens"],
+                       qs, 0.1, 1)
     k = torch.empty(3, 2, 32, 64, dtype=torch.bfloat16)
     L.contig_args(t["out"], t["q"], k, k.clone(), t["ctx_lens"], 0.1)
     with pytest.raises(ValueError):
         L.contig_args(t["out"], t["q"], k, torch.empty(3, 2, 16, 64, dtype=torch.bfloat16), t["ctx_lens"], 0.1)
+    with pytest.raises(ValueError, match="cache dtype"):
+        L.contig_args(t["out"], t["q"].float(), k, k.clone(), t["ctx_lens"], 0.1)
     with pytest.raises(ValueError):
         L.contig_args(t["out"], t["q"], torch.empty(4, 2, 32, 64, dtype=torch.bfloat16),
                       torch.empty(4, 2, 32, 64, dtype=torch.bfloat16), t["ctx_lens"], 0.1)
