@@ -23,7 +23,8 @@ Modules
 bits        decoding of raw fp32 / fp16 / bf16 bit patterns to float64
 capacity    block counts and KV byte accounting (pinned to printed numbers)
 pool_model  block pool: FIFO free list, refcounts, fork, copy-on-write
-kv_store    raw-bit KV cache in the [block][kv_head][slot][dim] layout
+kv_store    raw-bit KV cache in the [block][kv_head][slot][dim] layout, and
+            the host image of swapped-out blocks ([n][K, V][kv_head][slot][dim])
 attention   float64 gather-through-block-table decode attention, the
             contiguous-layout variant, and the split-context combine
 

@@ -1,8 +1,8 @@
 """Raw-bit KV cache model in the [block][kv_head][slot][dim] layout.
 
 Test infrastructure only.  Holds K and V as unsigned integer arrays of the
-element width, so every write and copy can be compared with the device cache
-byte for byte.  The layout is the reading this build takes of the pages'
+element width, so every write, copy and swap image can be compared with the
+device cache and the host buffer byte for byte.  The layout is the reading this build takes of the pages'
 statement that a block is contiguous inside and blocks may sit anywhere
 ("Paged Attention" (daiw.org), 定义): one block holds, per KV head, its B
 token rows of ``head_dim`` elements back to back.
@@ -47,3 +47,28 @@ class KVStoreModel:
         blocks = np.asarray(table, dtype=np.int64)[pos // self.block_size]
         rows = pos % self.block_size
         return self.k[blocks, :, rows, :], self.v[blocks, :, rows, :]
+
+    # -- swap images ("vllm-paged-attention-engine" (aiqz.cc), 连续批处理：
+    # 随到随走的新秩序: a preempted request's blocks are copied out to CPU
+    # memory and copied back in when it resumes).  The pages fix no host
+    # layout; the reading taken here is one record per listed block, in list
+    # order, holding that block's K and then its V, each in the cache's own
+    # [kv_head][slot][dim] order:  image[i][0] = K[blocks[i]],
+    # image[i][1] = V[blocks[i]].
+
+    def swap_image(self, blocks):
+        """Host image ``[n][2][kv_heads][B][head_dim]`` (raw bits) of the
+        listed blocks, K then V for each."""
+        n = len(blocks)
+        _, hkv, B, d = self.k.shape
+        image = np.empty((n, 2, hkv, B, d), dtype=self.k.dtype)
+        for i, blk in enumerate(blocks):
+            image[i, 0] = self.k[blk]
+            image[i, 1] = self.v[blk]
+        return image
+
+    def restore_image(self, blocks, image):
+        """Write a swap image back: block ``blocks[i]`` receives record i."""
+        for i, blk in enumerate(blocks):
+            self.k[blk] = image[i, 0]
+            self.v[blk] = image[i, 1]

@@ -54,6 +54,18 @@ class OracleRun:
         rows, lens = self.pool.block_tables(wl.batch, wl.max_blocks)
         return np.asarray(rows, dtype=np.int32), np.asarray(lens, dtype=np.int32)
 
+    # preemption: the pool's swap verbs plus the cache's swap images
+    def swap_out(self, seq):
+        """Release seq's blocks; returns (old table, host image of its blocks)."""
+        table = self.pool.swap_out(seq)
+        return table, self.cache.swap_image(table)
+
+    def swap_in(self, seq, image):
+        """New blocks for seq, filled from its image; returns the new table."""
+        table = self.pool.swap_in(seq)
+        self.cache.restore_image(table, image)
+        return table
+
 
 def logical_streams(wl):
     """seq -> row indices (into k_rows / v_rows) of its tokens, in order."""
