@@ -401,6 +401,28 @@ pa_status pa_decode_workspace_bytes(const pa_decode_args* args, size_t* bytes_ou
 pa_status pa_decode(const pa_decode_args* args, pa_stream stream);
 
 /*
+ * pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split-context records go to a static device array inside the library
+ * instead of a caller workspace; args->workspace and workspace_bytes are
+ * ignored.  The call allocates nothing.
+ *
+ * Limit: pa_decode_static_max_bytes() bytes (64 MiB).  A batch whose
+ * pa_decode_workspace_bytes exceeds it is refused with PA_E_UNSUPPORTED
+ * before anything is launched.  Each GPU the library runs on holds one such
+ * array until the process ends.
+ *
+ * Sharing: every call on one GPU uses that GPU's array, which keeps the last
+ * call's contents.  The contents need no initialisation, since each call
+ * rewrites all it reads.  Calls ordered on one stream are safe.  Two calls
+ * that may run at the same time on one GPU (different streams, no ordering
+ * between them) race on the array and give undefined results.  Otherwise the
+ * same as pa_decode: same checks, same kernels, bit-identical output.
+ */
+size_t pa_decode_static_max_bytes(void);
+pa_status pa_decode_static(const pa_decode_args* args, pa_stream stream);
+
+/*
  * Chunked prefill attention.  Sequence s holds ctx_lens[s] cached tokens, the
  * last n_s = q_start[s+1] - q_start[s] of which are the chunk being
  * prefilled: their K/V rows have been written (pa_write_kv) before the call.

@@ -117,6 +117,8 @@ _SIGS = {
     "pa_swap_in": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_i32, [ctypes.POINTER(pa_decode_args), ctypes.POINTER(c_sz)]),
     "pa_decode": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
+    "pa_decode_static_max_bytes": (c_sz, []),
+    "pa_decode_static": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
     "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
     "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
     "pa_decode_set_waves": (c_i32, [c_i32]),
@@ -481,6 +483,27 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0
             a.workspace_bytes = workspace.numel()
     check(_lib.pa_decode(ctypes.byref(a), stream if stream is not None else current_stream()), "pa_decode")
     return workspace
+
+
+def pa_decode_static_max_bytes():
+    """Size of the library's static split-context array (bytes)."""
+    return int(_lib.pa_decode_static_max_bytes())
+
+
+def pa_decode_static(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx=0,
+                     partition_size=0, stream=None, k_scale=1.0, v_scale=1.0):
+    """pa_decode without a workspace: the library's static device array holds
+    the split-context records, so nothing is allocated.  Calls that may
+    overlap on one GPU must not be issued (they share the array)."""
+    for t, dt in ((block_tables, torch.int32), (ctx_lens, torch.int32)):
+        if t.dtype != dt:
+            raise ValueError("block_tables and ctx_lens must be int32")
+    for t in (out, q, k_cache, v_cache, block_tables, ctx_lens):
+        _dev(t)
+    a = decode_args(out, q, k_cache, v_cache, block_tables, ctx_lens, scale, max_ctx, partition_size,
+                    None, k_scale, v_scale)
+    check(_lib.pa_decode_static(ctypes.byref(a), stream if stream is not None else current_stream()),
+          "pa_decode_static")
 
 
 def contig_args(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_size=0, workspace=None):

@@ -1281,6 +1281,36 @@ pa_status debug_validate(const pa_decode_args* a, int max_ctx, hipStream_t st) {
   return ok();
 }
 
+// ---- allocation-free decode ------------------------------------------------
+//
+// For callers that may not allocate device memory: the split-context records
+// go to a file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy of the array until the process ends.
+// The host-side name of the array is not a device address, so its address on
+// each device is looked up once (hipGetSymbolAddress, with that device
+// current) and only that pointer is handed to kernels.
+
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+pa_status static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> by_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_E_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it == by_device.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    it = by_device.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return ok();
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -1365,6 +1395,27 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   }
   return launch<true>(p, plan, a->kv_dtype, a->head_dim, G, a->num_seqs,
                       a->num_kv_heads, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t pa_decode_static_max_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" pa_status pa_decode_static(const pa_decode_args* a, pa_stream stream) {
+  Plan plan;
+  pa_status st = check_paged(a, &plan);
+  if (st != PA_OK) return st;
+  if (plan.workspace > kStaticScratchBytes)
+    return fail(PA_E_UNSUPPORTED, "this batch needs " + std::to_string(plan.workspace) +
+                                      " bytes of split-context records, above the static maximum of " +
+                                      std::to_string(kStaticScratchBytes));
+  pa_decode_args local = *a;
+  local.workspace = nullptr;
+  local.workspace_bytes = 0;
+  if (plan.workspace > 0 && a->num_seqs > 0) {
+    st = static_scratch(&local.workspace);
+    if (st != PA_OK) return st;
+    local.workspace_bytes = kStaticScratchBytes;
+  }
+  return pa_decode(&local, stream);
 }
 
 extern "C" pa_status pa_decode_contiguous_workspace_bytes(const pa_contig_args* a, size_t* bytes_out) {

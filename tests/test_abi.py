@@ -345,3 +345,19 @@ def test_cache_ops_refuse_mismatched_v_cache():
     k8 = torch.empty(4, 2, 16, 64, dtype=torch.uint8)
     with pytest.raises(ValueError, match="same shape"):
         L.pa_write_kv_fp8(k8, k8[:, :, :8].contiguous(), rows, rows, slots, 1.0, 1.0)
+
+
+def test_static_decode_refuses_batches_beyond_its_array_before_launch():
+    # pa_decode_static has a fixed 64 MiB array for the split-context records
+    lib = P.raw()
+    assert lib.pa_decode_static_max_bytes() == 64 << 20
+    big = _args(num_seqs=4096, max_blocks=512, partition_size=512)     # 4096 x 32 heads x 16 partitions
+    n = ctypes.c_size_t()
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > 64 << 20
+    assert lib.pa_decode_static(ctypes.byref(big), None) == L.PA_E_UNSUPPORTED
+    assert b"static maximum" in lib.pa_last_error()
+    # argument errors are reported as by pa_decode
+    assert lib.pa_decode_static(ctypes.byref(_args(head_dim=96)), None) == L.PA_E_UNSUPPORTED
+    assert lib.pa_decode_static(ctypes.byref(_args(q_dtype=L.PA_F32)), None) == L.PA_E_INVAL
+    assert lib.pa_decode_static(ctypes.byref(_args(num_seqs=0)), None) == 0
