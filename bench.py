@@ -11,21 +11,26 @@ caches.
 
 Prints ONE JSON line (rank 0, N = 1): value = logical KV bytes read per step
 / step time (GB/s).  ``roofline`` is measured live with HIP events around
-every pa_decode launch in the timed region; ``cpu_baseline`` times the float64
-oracle on a bounded sample of the same batch.
+every pa_decode call in the timed region (partition + combine launches);
+beside its algorithmic ``frac`` it carries ``hbm_frac`` (the call's HBM bytes
+from the committed rocprofv3 counter summary, over the same time) and the
+rate of unique KV bytes.  ``cpu_baseline`` times the float64 oracle on every
+available host core.
 
-The line also carries a ``prefill`` object: pa_prefill (chunked causal
-prefill over the paged cache) on the Llama-3.1-8B-like prefill batch (16
-sequences, 512-token chunks after cached prefixes of 0..2048 tokens), in
-algorithmic TFLOP/s against the dense bf16 matrix-core peak, with its own
-roofline and oracle baseline.  ``--mode prefill`` prints that object alone.
-``prefix_cache`` and ``swap`` measure the prefix cache and the preemption
-copies; ``fp8`` runs the same decode step over an E4M3 copy of the cache
-(pa_write_kv_fp8 of the new tokens, pa_decode over codes), with its own
-roofline and oracle baseline.  ``--mode prefix|swap|fp8`` prints one alone.
+Nested objects in the same line:
+  noshare      the same step with every prefix private (logical = unique
+               bytes), with its own roofline and oracle baseline;
+  block_sweep  B = 8 / 16 / 32 at ctx 1000 x 128: paged, contiguous-layout
+               and identity-placement pa_decode times and the overheads;
+  ceiling      plain streaming read and scattered 4 KiB-tile read rates;
+  prefill      pa_prefill on the Llama-3.1-8B-like prefill batch, TFLOP/s
+               against the dense bf16 matrix-core peak;
+  prefix_cache, swap, fp8   the prefix cache, the preemption copies, and the
+               decode step over an E4M3 copy of the cache.
+``--mode decode|prefill|prefix|swap|fp8|ceiling`` prints one alone.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--mode decode|prefill|prefix|swap|fp8] [--no-prefill]
+                    [--mode ...] [--no-extras]
 """
 import argparse
 import hashlib
@@ -128,32 +133,77 @@ def host_cpu():
     return {"cpu_model": model, "cores_available": avail}
 
 
-def cpu_baseline(wl, budget_s=10.0):
-    """The float64 oracle, as it stands, on the first sequences of the batch
-    until ~budget_s of work; scaled to GB/s of logical KV."""
+# ---- CPU baselines --------------------------------------------------------------
+# The oracle runs in processes forked from this one, one per available core,
+# before anything initialises the GPU (a process that holds the GPU is never
+# forked).  Each process sees the parent's arrays copy-on-write, runs with one
+# BLAS thread, and works on its own share of the sequences.
+
+_FORK = {}
+
+
+def _one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _noop(_):
+    return None
+
+
+def fork_map(worker, chunks, min_wall=2.0, max_reps=16):
+    """Runs worker(chunk) over all chunks on one forked process per available
+    core; repeats the whole map until ~min_wall seconds.  Returns (wall time
+    of one map, cores used, repetitions)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    cores = host_cpu()["cores_available"]
+    with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("fork"), initializer=_one_thread) as ex:
+        list(ex.map(_noop, range(4 * cores)))          # every worker started before timing
+        walls = []
+        while not walls or (sum(walls) < min_wall and len(walls) < max_reps):
+            t0 = time.perf_counter()
+            list(ex.map(worker, chunks))
+            walls.append(time.perf_counter() - t0)
+    return min(walls), cores, len(walls)
+
+
+def _chunks(n, parts):
+    step = max(1, -(-n // parts))
+    return [slice(a, min(n, a + step)) for a in range(0, n, step)]
+
+
+def _decode_chunk(sl):
+    from oracle import attention as A
+    st = _FORK["decode"]
+    A.paged_decode(st["q"][sl], st["k"], st["v"], st["tables"][sl], st["lens"][sl], st["B"], st["scale"],
+                   st["dtype"], st["Hq"], st["Hkv"])
+
+
+def cpu_baseline(wl):
+    """The float64 oracle, as it stands, over the whole batch on every
+    available core; GB/s of logical KV."""
     import numpy as np
 
-    from oracle import attention as A
     from tests._replay import OracleRun
     run = OracleRun(wl)
     tables, lens = run.tables(wl)
-    e = elem_bytes(wl.dtype)
-    done, kv, wall, cpu = 0, 0, 0.0, 0.0
-    while done < wl.num_seqs and wall < budget_s:
-        n = min(8, wl.num_seqs - done)
-        sl = slice(done, done + n)
-        t0, c0 = time.perf_counter(), time.process_time()
-        A.paged_decode(wl.q[sl], run.cache.k, run.cache.v, tables[sl], lens[sl], wl.block_size,
-                       wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        kv += int(np.sum(lens[sl])) * 2 * wl.num_kv_heads * wl.head_dim * e
-        done += n
-    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB logical KV), "
-                      f"{wall:.1f} s wall, float64 numpy",
-            "seqs_per_s": round(done / wall, 2), **host_cpu()}
+    _FORK["decode"] = dict(q=wl.q, k=run.cache.k, v=run.cache.v, tables=tables, lens=lens, B=wl.block_size,
+                           scale=wl.scale, dtype=wl.dtype, Hq=wl.num_q_heads, Hkv=wl.num_kv_heads)
+    # longest sequences first, in small chunks, so the processes finish together
+    order = np.argsort(-lens, kind="stable")
+    _FORK["decode"].update(q=wl.q[order], tables=tables[order], lens=lens[order])
+    cores = host_cpu()["cores_available"]
+    wall, cores, reps = fork_map(_decode_chunk, _chunks(wl.num_seqs, 8 * cores))
+    kv = int(np.sum(lens)) * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl.dtype)
+    del _FORK["decode"]
+    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {wl.num_seqs} sequences ({kv / 1e9:.3f} GB logical KV) on {cores} forked processes, "
+                      f"{wall:.2f} s wall (best of {reps}), float64 numpy",
+            "seqs_per_s": round(wl.num_seqs / wall, 2), **host_cpu()}
 
 
 def prefill_flops(ctx, q_start, head_dim, num_q_heads):
@@ -169,34 +219,43 @@ def prefill_flops(ctx, q_start, head_dim, num_q_heads):
     return total * 4 * head_dim * num_q_heads
 
 
-def prefill_cpu_baseline(wl, budget_s=10.0):
-    """The float64 prefill oracle, as it stands, on whole sequences of the
-    batch (all rows, all heads) until ~budget_s of work; in TFLOP/s."""
-    import numpy as np
-
+def _prefill_chunk(job):
     from oracle import prefill as PF
+    st = _FORK["prefill"]
+    s, r0, r1 = job
+    rows = [(r, h) for r in range(r0, r1) for h in range(st["Hq"])]
+    PF.paged_prefill(st["q_rows"], st["k"], st["v"], st["tables"], st["lens"], st["qs"], st["B"], st["scale"],
+                     st["dtype"], st["Hq"], st["Hkv"], rows=rows)
+
+
+def prefill_cpu_baseline(wl):
+    """The float64 prefill oracle, as it stands, over the whole batch (every
+    chunk row and head) on every available core; TFLOP/s."""
     from tests._replay import OracleRun
     run = OracleRun(wl)
     tables, lens = run.tables(wl)
-    qs = wl.info["q_start"]
-    done, flops, wall, cpu = 0, 0, 0.0, 0.0
-    while done < wl.num_seqs and wall < budget_s:
-        s = done
-        rows = [(r, h) for r in range(qs[s], qs[s + 1]) for h in range(wl.num_q_heads)]
-        t0, c0 = time.perf_counter(), time.process_time()
-        PF.paged_prefill(wl.info["q_rows"], run.cache.k, run.cache.v, tables, lens, qs, wl.block_size,
-                         wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads, rows=rows)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        flops += prefill_flops(lens[s:s + 1], [0, qs[s + 1] - qs[s]], wl.head_dim, wl.num_q_heads)
-        done += 1
-    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"first {done} of {wl.num_seqs} sequences, every chunk row and head "
-                      f"({flops / 1e9:.2f} GFLOP), {wall:.1f} s wall, float64 numpy", **host_cpu()}
+    qs = [int(x) for x in wl.info["q_start"]]
+    _FORK["prefill"] = dict(q_rows=wl.info["q_rows"], k=run.cache.k, v=run.cache.v, tables=tables, lens=lens,
+                            qs=qs, B=wl.block_size, scale=wl.scale, dtype=wl.dtype, Hq=wl.num_q_heads,
+                            Hkv=wl.num_kv_heads)
+    jobs = []
+    for s in range(wl.num_seqs):                 # 32-row jobs
+        jobs += [(s, r, min(r + 32, qs[s + 1])) for r in range(qs[s], qs[s + 1], 32)]
+    jobs = jobs[::4]                             # a bounded sample: every fourth job, every head
+    jobs.sort(key=lambda j: -int(lens[j[0]]))    # longest contexts first
+    wall, cores, reps = fork_map(_prefill_chunk, jobs, min_wall=1.0, max_reps=2)
+    del _FORK["prefill"]
+    d, Hq = wl.head_dim, wl.num_q_heads
+    # a chunk row at position p costs (p + 1) dot products and (p + 1) multiply-adds of d, per head
+    flops = sum(4 * d * Hq * (int(lens[s]) - (qs[s + 1] - qs[s]) + (r - qs[s]) + 1)
+                for s, r0, r1 in jobs for r in range(r0, r1))
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"every fourth 32-row job of the {wl.num_seqs}-sequence batch, every head "
+                      f"({flops / 1e9:.1f} GFLOP) on {cores} forked processes, {wall:.2f} s wall (best of {reps}), "
+                      f"float64 numpy", **host_cpu()}
 
 
-def bench_prefill(steps, warmup, dev, with_cpu):
+def bench_prefill(wl, steps, warmup, dev, cpu=None):
     """pa_prefill on the Llama-3.1-8B-like prefill batch: each launch timed
     with HIP events on the stream it runs on."""
     import numpy as np
@@ -205,7 +264,6 @@ def bench_prefill(steps, warmup, dev, with_cpu):
     import paged_kv_cache_147_amd as P
     import workloads as W
     from tests._native import NativeDeviceRun, device_tensor
-    wl = W.llama31_8b_prefill()
     run = NativeDeviceRun(wl, device=dev)
     ctx = run.ctx_host.tolist()
     qs = [int(x) for x in wl.info["q_start"]]
@@ -260,11 +318,8 @@ def bench_prefill(steps, warmup, dev, with_cpu):
                      "traffic": measured_prefill_traffic(), "kernel": "pa_prefill (one launch)",
                      "avg_launch_ms": round(avg, 5), "flops_per_launch": flops,
                      "launch_ms_p10_median_p90": [round(float(np.percentile(ms, x)), 5) for x in (10, 50, 90)]},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if with_cpu:
-        log("[bench] timing the prefill oracle on a CPU sample ...")
-        res["cpu_baseline"] = prefill_cpu_baseline(wl)
     return res
 
 
@@ -478,10 +533,39 @@ def measured_fp8_traffic(workload):
     return float(m.group(2))
 
 
-def fp8_cpu_baseline(wl, k_scale, v_scale, budget_s=10.0):
-    """oracle.fp8.paged_decode_fp8, as it stands, on the first sequences of the
-    batch until ~budget_s of work (codes quantised by the oracle beforehand,
-    untimed); scaled to GB/s of code bytes."""
+def _fp8_chunk(sl):
+    from oracle import fp8 as F
+    st = _FORK["fp8"]
+    F.paged_decode_fp8(st["q"][sl], st["dtype"], st["k"], st["v"], st["ks"], st["vs"], st["tables"][sl],
+                       st["lens"][sl], st["B"], st["scale"], st["Hq"], st["Hkv"])
+
+
+def _shared_u8(shape):
+    """A zeroed uint8 array in anonymous shared memory: forked processes
+    write into it and the parent sees the result."""
+    import mmap
+
+    import numpy as np
+    n = int(np.prod(shape))
+    return np.frombuffer(mmap.mmap(-1, max(n, 1)), dtype=np.uint8)[:n].reshape(shape)
+
+
+def _quantize_chunk(sl):
+    """E4M3 codes (the oracle's quantisation) of a slice of the used blocks."""
+    import numpy as np
+
+    from oracle import fp8 as F
+    from oracle.bits import to_f64
+    st = _FORK["quant"]
+    ids = st["used"][sl]
+    st["kc"][ids] = F.quantize(to_f64(st["k"][ids], st["dtype"]).astype(np.float32), st["ks"])
+    st["vc"][ids] = F.quantize(to_f64(st["v"][ids], st["dtype"]).astype(np.float32), st["vs"])
+
+
+def fp8_cpu_baseline(wl, k_scale, v_scale):
+    """oracle.fp8.paged_decode_fp8, as it stands, over the whole batch on
+    every available core (codes quantised by the oracle beforehand,
+    untimed); GB/s of code bytes."""
     import numpy as np
 
     from oracle import fp8 as F
@@ -489,27 +573,26 @@ def fp8_cpu_baseline(wl, k_scale, v_scale, budget_s=10.0):
     from tests._replay import OracleRun
     run = OracleRun(wl)
     tables, lens = run.tables(wl)
-    kc = F.quantize(to_f64(run.cache.k, wl.dtype).astype(np.float32), k_scale)
-    vc = F.quantize(to_f64(run.cache.v, wl.dtype).astype(np.float32), v_scale)
-    done, kv, wall, cpu = 0, 0, 0.0, 0.0
-    while done < wl.num_seqs and wall < budget_s:
-        n = min(8, wl.num_seqs - done)
-        sl = slice(done, done + n)
-        t0, c0 = time.perf_counter(), time.process_time()
-        F.paged_decode_fp8(wl.q[sl], wl.dtype, kc, vc, k_scale, v_scale, tables[sl], lens[sl], wl.block_size,
-                           wl.scale, wl.num_q_heads, wl.num_kv_heads)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        kv += int(np.sum(lens[sl])) * 2 * wl.num_kv_heads * wl.head_dim
-        done += n
-    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"first {done} of {wl.num_seqs} sequences ({kv / 1e9:.3f} GB of codes), "
-                      f"{wall:.1f} s wall, float64 numpy",
-            "seqs_per_s": round(done / wall, 2), **host_cpu()}
+    used = np.unique(tables[tables >= 0])
+    kc, vc = _shared_u8(run.cache.k.shape), _shared_u8(run.cache.v.shape)
+    _FORK["quant"] = dict(k=run.cache.k, v=run.cache.v, kc=kc, vc=vc, used=used, dtype=wl.dtype, ks=k_scale,
+                          vs=v_scale)
+    fork_map(_quantize_chunk, _chunks(len(used), 4 * host_cpu()["cores_available"]), min_wall=0.0, max_reps=1)
+    del _FORK["quant"]
+    order = np.argsort(-lens, kind="stable")
+    _FORK["fp8"] = dict(q=wl.q[order], dtype=wl.dtype, k=kc, v=vc, ks=k_scale, vs=v_scale, tables=tables[order],
+                        lens=lens[order], B=wl.block_size, scale=wl.scale, Hq=wl.num_q_heads, Hkv=wl.num_kv_heads)
+    cores = host_cpu()["cores_available"]
+    wall, cores, reps = fork_map(_fp8_chunk, _chunks(wl.num_seqs, 8 * cores))
+    del _FORK["fp8"]
+    kv = int(np.sum(lens)) * 2 * wl.num_kv_heads * wl.head_dim
+    return {"value": round(kv / wall / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {wl.num_seqs} sequences ({kv / 1e9:.3f} GB of codes) on {cores} forked processes, "
+                      f"{wall:.2f} s wall (best of {reps}), float64 numpy",
+            "seqs_per_s": round(wl.num_seqs / wall, 2), **host_cpu()}
 
 
-def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, with_cpu, bf16_decode_ms=None,
+def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode_ms=None,
               k_scale=1 / 56, v_scale=1 / 72, partition_size=0):
     """The decode step over an E4M3 cache: the bf16 cache of the same batch is
     quantised once (pa_write_kv_fp8 over every slot, untimed), then each step
@@ -595,11 +678,8 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, with_cpu, bf16_decode
                      "kernel": "pa_decode over E4M3 codes (partition + combine launches)",
                      "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg,
                      "launch_ms_p10_median_p90": [round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)]},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if with_cpu:
-        log("[bench] timing the E4M3 oracle on a CPU sample ...")
-        res["cpu_baseline"] = fp8_cpu_baseline(wl, k_scale, v_scale)
     return res
 
 
@@ -630,142 +710,47 @@ def time_calls(fn, n, warm=5):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def compare_contiguous(wl, run, replicas, ws_paged, args, stream):
-    """Paged decode vs the same attention on the contiguous layout (identical
-    logical K/V), and vs the paged kernel with blocks placed in order; all
-    three timed the same way (pa_decode* alone, rotating cache copies)."""
+def unique_kv_bytes(wl, tables, ctx):
+    """KV bytes of the distinct token rows a batch reads (shared prefix
+    blocks count once)."""
+    import numpy as np
+    B = wl.block_size
+    slots = []
+    for s, c in enumerate(ctx):
+        pos = np.arange(int(c))
+        slots.append(tables[s, pos // B].astype(np.int64) * B + pos % B)
+    n = len(np.unique(np.concatenate(slots))) if slots else 0
+    return n * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl.dtype)
+
+
+def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_size=0, cpu=None):
+    """One decode step (copies, pa_write_kv of the new tokens, pa_decode),
+    timed over `steps` steps after `warmup`; every pa_decode call between HIP
+    events on the stream it runs on.  Returns (result, device run, average
+    pa_decode ms)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_147_amd as P
-    from tests._native import NativeDeviceRun, device_tensor
-    from tests._replay import contiguous_layout
-    dev = run.q.device
-    ctx = run.ctx_host
-    cap = int((ctx.max() + 7) // 8 * 8)
-    k, v, _ = contiguous_layout(wl, capacity=cap)
-    reps = [(device_tensor(k, wl.dtype, dev), device_tensor(v, wl.dtype, dev))]
-    for _ in range(args.replicas - 1):
-        reps.append((reps[0][0].clone(), reps[0][1].clone()))
-    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
-    ws = [None]
-
-    def paged(i):
-        kc, vc = replicas[i % len(replicas)]
-        P.pa_decode(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=int(ctx.max()),
-                    partition_size=args.partition_size, workspace=ws_paged, stream=stream)
-    paged_ms = time_calls(paged, args.steps)
-
-    def contig(i):
-        kc, vc = reps[i % len(reps)]
-        ws[0] = P.pa_decode_contiguous(out, run.q, kc, vc, run.ctx, wl.scale, max_ctx=int(ctx.max()),
-                                       partition_size=args.partition_size, workspace=ws[0], stream=stream)
-    contig_ms = time_calls(contig, args.steps)
-    del reps
-    # paged kernel, blocks in table order (free list 0..n-1): same lookups, contiguous placement
-    wl_id = type(wl)(**{**wl.__dict__, "free_order": np.arange(wl.num_blocks, dtype=np.int32)})
-    run_id = NativeDeviceRun(wl_id, device=dev)
-    reps_id = [(run_id.k_cache, run_id.v_cache)] + [(run_id.k_cache.clone(), run_id.v_cache.clone())
-                                                   for _ in range(args.replicas - 1)]
-    ws_id = [None]
-
-    def paged_identity(i):
-        kc, vc = reps_id[i % len(reps_id)]
-        ws_id[0] = P.pa_decode(out, run_id.q, kc, vc, run_id.tables, run_id.ctx, wl.scale,
-                               max_ctx=int(ctx.max()), partition_size=args.partition_size,
-                               workspace=ws_id[0], stream=stream)
-    ident_ms = time_calls(paged_identity, args.steps)
-    return {"paged_ms": round(paged_ms, 5), "contiguous_ms": round(contig_ms, 5),
-            "paged_identity_placement_ms": round(ident_ms, 5),
-            "overhead_vs_contiguous": round(paged_ms / contig_ms - 1, 4),
-            "overhead_identity_vs_contiguous": round(ident_ms / contig_ms - 1, 4)}
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama31_8b_gqa", choices=sorted(WORKLOADS))
-    ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
-    ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "prefill", "prefix", "swap", "fp8"), default="decode",
-                    help="prefill / prefix: print only the pa_prefill / prefix-cache measurement")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="leave the prefill, prefix-cache, swap and fp8 objects out")
-    ap.add_argument("--prefill-steps", type=int, default=50)
-    ap.add_argument("--prefill-warmup", type=int, default=200,
-                    help="untimed pa_prefill launches before the timed ones (~60 ms: the matrix-core "
-                         "clock takes that long to settle; 10 launches read ~15%% slow)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--compare-contiguous", action="store_true",
-                    help="also time pa_decode_contiguous on the same logical K/V and the paged "
-                         "kernel with blocks placed in order (identity free list); adds a "
-                         "'paged_vs_contiguous' object to the JSON line")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
-              "(use --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import paged_kv_cache_147_amd as P
-    import workloads as W
     from tests._native import NativeDeviceRun
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    if args.mode == "swap":
-        res = bench_swap(dev, not args.no_cpu_baseline)
-        res.update({"n_gpus": 1, "vs_baseline": None})
-        print(json.dumps(res), flush=True)
-        return
-    if args.mode == "prefix":
-        res = bench_prefix(dev, not args.no_cpu_baseline)
-        res.update({"n_gpus": 1, "vs_baseline": None})
-        print(json.dumps(res), flush=True)
-        return
-    if args.mode == "prefill":
-        res = bench_prefill(args.prefill_steps, args.prefill_warmup, dev, not args.no_cpu_baseline)
-        if args.copy_calibration:
-            copy_calibration(dev)
-        res.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
-        print(json.dumps(res), flush=True)
-        return
-    key, desc = WORKLOADS[args.workload]
     t0 = time.time()
-    wl = W.CONFIGS[key]()
-    log(f"[bench] workload {wl.name}: generated in {time.time() - t0:.1f}s")
     run = NativeDeviceRun(wl, device=dev)
     ctx = run.ctx_host.tolist()
     kv_bytes, alg_bytes = decode_bytes(wl, ctx)
-    log(f"[bench] cache built; {wl.num_seqs} seqs, KV {kv_bytes / 1e9:.3f} GB logical")
-    if args.mode == "fp8":
-        res = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas,
-                        not args.no_cpu_baseline, partition_size=args.partition_size)
-        if args.copy_calibration:
-            copy_calibration(dev)
-        res.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
-        print(json.dumps(res), flush=True)
-        return
-
-    # The step's own work: copies, then one write of every new token.
+    uniq = unique_kv_bytes(wl, run.tables.cpu().numpy(), ctx)
+    log(f"[bench] {workload}: cache built in {time.time() - t0:.1f}s; {wl.num_seqs} seqs, KV {kv_bytes / 1e9:.3f} GB "
+        f"logical, {uniq / 1e9:.3f} GB unique")
     step_rows = torch.cat([torch.arange(r0, r0 + n) for (_, r0, n) in run.step_writes]).to(dev)
     step_slots = torch.cat([s for (s, _, _) in run.step_writes])
     k_new = run.k_rows.index_select(0, step_rows).contiguous()
     v_new = run.v_rows.index_select(0, step_rows).contiguous()
-    pairs = (torch.tensor(run.step_copies, dtype=torch.int32, device=dev)
-             if run.step_copies else None)
+    pairs = (torch.tensor(run.step_copies, dtype=torch.int32, device=dev) if run.step_copies else None)
     replicas = [(run.k_cache, run.v_cache)]
-    for _ in range(args.replicas - 1):
+    for _ in range(nrep - 1):
         replicas.append((run.k_cache.clone(), run.v_cache.clone()))
     out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     probe = P._lib.decode_args(out, run.q, run.k_cache, run.v_cache, run.tables, run.ctx, wl.scale,
-                               max_ctx=max(ctx), partition_size=args.partition_size)
+                               max_ctx=max(ctx), partition_size=partition_size)
     ws = P._lib.workspace_for(P.pa_decode_workspace_bytes(probe), dev)
     stream = P.current_stream(dev)
 
@@ -777,76 +762,325 @@ def main():
         if ev is not None:
             ev[0].record()
         P.pa_decode(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=max(ctx),
-                    partition_size=args.partition_size, workspace=ws, stream=stream)
+                    partition_size=partition_size, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for i in range(steps):
+        step(warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     dec_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = elapsed * 1e3 / args.steps
+    ms_step = elapsed * 1e3 / steps
     dec_avg = float(np.mean(dec_ms))
-    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; pa_decode avg {dec_avg:.4f} ms "
+    log(f"[bench] {workload}: {steps} steps: {ms_step:.4f} ms/step; pa_decode avg {dec_avg:.4f} ms "
         f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
-
-    if args.copy_calibration:
-        copy_calibration(dev)
-
-    comparison = None
-    if args.compare_contiguous:
-        comparison = compare_contiguous(wl, run, replicas, ws, args, stream)
-
     gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
-    result = {
+    traffic = measured_traffic(workload)
+    hbm_gbps = traffic / (dec_avg * 1e-3) / 1e9 if traffic else None
+    res = {
         "metric": METRIC,
         "value": round(gbps, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": wl.dtype,
+        "accumulate": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "description": desc, "batch": wl.num_seqs,
+        "config": {"workload": workload, "description": desc, "batch": wl.num_seqs,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.dtype,
                    "out_dtype": "f32", "ctx_mean": round(float(np.mean(ctx)), 1),
-                   "ctx_max": int(max(ctx)), "kv_bytes_per_step": kv_bytes,
-                   "cache_replicas": len(replicas), "parallelism": "single GPU"},
+                   "ctx_max": int(max(ctx)), "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq,
+                   "cache_replicas": len(replicas), "partition_size": partition_size,
+                   "parallelism": "single GPU"},
+        "logical_kv_gbps": round(gbps, 2),
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "seqs_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
+        "decode_seqs_per_s": round(wl.num_seqs / (dec_avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (partition + combine launches)",
+                     "traffic": traffic,
+                     "hbm_gbps": round(hbm_gbps, 2) if hbm_gbps else None,
+                     "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4) if hbm_gbps else None,
+                     "unique_kv_gbps": round(uniq / (dec_avg * 1e-3) / 1e9, 2),
+                     "kernel": "pa_decode (partition + combine launches)",
                      "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg_bytes,
                      "launch_ms_p10_median_p90": [round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)]},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if comparison is not None:
-        result["paged_vs_contiguous"] = comparison
-    if not args.no_prefill:
-        result["prefill"] = bench_prefill(args.prefill_steps, args.prefill_warmup, dev, not args.no_cpu_baseline)
-        result["prefix_cache"] = bench_prefix(dev, not args.no_cpu_baseline)
-        result["swap"] = bench_swap(dev, not args.no_cpu_baseline)
+    del replicas
+    return res, run, dec_avg
+
+
+def time_contiguous(wl, run, steps, nrep, dev, partition_size=0):
+    """pa_decode vs the same attention on the contiguous layout (identical
+    logical K/V), and vs the paged kernel with its blocks placed in table
+    order (identity free list: the same lookups over contiguous memory); all
+    three timed alike (the decode call alone, rotating cache copies)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    from tests._native import NativeDeviceRun, device_tensor
+    from tests._replay import contiguous_layout
+    stream = P.current_stream(dev)
+    ctx = run.ctx_host
+    mctx = int(ctx.max())
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    reps = [(run.k_cache, run.v_cache)] + [(run.k_cache.clone(), run.v_cache.clone()) for _ in range(nrep - 1)]
+    ws = [None]
+
+    def paged(i):
+        kc, vc = reps[i % len(reps)]
+        ws[0] = P.pa_decode(out, run.q, kc, vc, run.tables, run.ctx, wl.scale, max_ctx=mctx,
+                            partition_size=partition_size, workspace=ws[0], stream=stream)
+    paged_ms = time_calls(paged, steps)
+    del reps
+    cap = (mctx + 7) // 8 * 8
+    k, v, _ = contiguous_layout(wl, capacity=cap)
+    creps = [(device_tensor(k, wl.dtype, dev), device_tensor(v, wl.dtype, dev))]
+    del k, v
+    creps += [(creps[0][0].clone(), creps[0][1].clone()) for _ in range(nrep - 1)]
+    wsc = [None]
+
+    def contig(i):
+        kc, vc = creps[i % len(creps)]
+        wsc[0] = P.pa_decode_contiguous(out, run.q, kc, vc, run.ctx, wl.scale, max_ctx=mctx,
+                                        partition_size=partition_size, workspace=wsc[0], stream=stream)
+    contig_ms = time_calls(contig, steps)
+    del creps
+    wl_id = type(wl)(**{**wl.__dict__, "free_order": np.arange(wl.num_blocks, dtype=np.int32)})
+    run_id = NativeDeviceRun(wl_id, device=dev)
+    ireps = [(run_id.k_cache, run_id.v_cache)] + [(run_id.k_cache.clone(), run_id.v_cache.clone())
+                                                 for _ in range(nrep - 1)]
+    wsi = [None]
+
+    def paged_identity(i):
+        kc, vc = ireps[i % len(ireps)]
+        wsi[0] = P.pa_decode(out, run_id.q, kc, vc, run_id.tables, run_id.ctx, wl.scale, max_ctx=mctx,
+                             partition_size=partition_size, workspace=wsi[0], stream=stream)
+    ident_ms = time_calls(paged_identity, steps)
+    del ireps, run_id
+    return {"paged_ms": round(paged_ms, 5), "contiguous_ms": round(contig_ms, 5),
+            "paged_identity_placement_ms": round(ident_ms, 5),
+            "overhead_vs_contiguous": round(paged_ms / contig_ms - 1, 4),
+            "overhead_identity_vs_contiguous": round(ident_ms / contig_ms - 1, 4)}
+
+
+def bench_block_sweep(dev, steps, nrep):
+    """Block sizes 8 / 16 / 32 on 128 sequences at ctx 1000 (GQA 32 / 8, d 128,
+    bf16, identical logical Q/K/V for every B): the paged call, the
+    contiguous-layout call and the identity-placement call, decode only."""
+    import torch
+
+    import workloads as W
+    rows = {}
+    for B in (8, 16, 32):
+        wl = W.block_sweep(B)
+        from tests._native import NativeDeviceRun
+        run = NativeDeviceRun(wl, device=dev)
+        kv, alg = decode_bytes(wl, run.ctx_host.tolist())
+        r = time_contiguous(wl, run, steps, nrep, dev)
+        r["paged_gbps"] = round(alg / (r["paged_ms"] * 1e-3) / 1e9, 2)
+        r["paged_frac"] = round(alg / (r["paged_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+        r["contiguous_gbps"] = round(alg / (r["contiguous_ms"] * 1e-3) / 1e9, 2)
+        r["blocks_per_seq"] = -(-1000 // B)
+        rows[f"B{B}"] = r
+        log(f"[bench] block sweep B={B}: paged {r['paged_ms']:.4f} ms, contiguous {r['contiguous_ms']:.4f} ms, "
+            f"identity {r['paged_identity_placement_ms']:.4f} ms ({100 * r['overhead_vs_contiguous']:+.1f}%)")
+        del run
+        torch.cuda.empty_cache()
+    return {"metric": "paged vs contiguous-layout pa_decode time (indirection overhead)",
+            "config": {"workload": "ctx 1000 x 128 sequences, GQA 32/8, d 128, bf16, B in {8, 16, 32}",
+                       "kv_bytes_per_call": kv, "calls_timed": steps, "cache_replicas": nrep},
+            **rows}
+
+
+def bench_ceiling(dev, reps=20):
+    """Read rates this GPU reaches with no arithmetic: a plain stream over
+    1 GiB, and whole 4 KiB tiles at scattered indices of a 4 GiB buffer
+    (the decode's (block, KV head) tile shape), 1 GiB read per launch; HIP
+    events around each launch."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_147_amd as P
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_147_amd", "libpagedkv_ceiling.so"))
+    lib.pc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pc_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    stream = P.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 1 << 30
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev), torch.full((nbytes,), 3, dtype=torch.uint8, device=dev)]
+    blocks = cus * 8
+    sink = torch.empty(blocks * 256 * 16, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            fn(i)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    def stream_read(i):
+        assert lib.pc_stream_read(bufs[i % 2].data_ptr(), nbytes, blocks, sink.data_ptr(), stream) == 0
+    ms_stream = timed(stream_read)
+    del bufs
+    tile = 4096
+    big = torch.ones(4 * nbytes, dtype=torch.uint8, device=dev)
+    n_tiles = nbytes // tile
+    rng = np.random.default_rng(0)
+    ids = [torch.from_numpy(rng.permutation(4 * nbytes // tile)[:n_tiles].astype(np.int32)).to(dev) for _ in range(2)]
+    per_wave = 4
+    tsink = torch.empty(-(-n_tiles // per_wave) * 64 * 16, dtype=torch.uint8, device=dev)
+
+    def tile_read(i):
+        assert lib.pc_tile_read(big.data_ptr(), ids[i % 2].data_ptr(), n_tiles, tsink.data_ptr(), stream) == 0
+    ms_tile = timed(tile_read)
+    del big
+    torch.cuda.empty_cache()
+    res = {"metric": "read rate with no arithmetic (context for the decode roofline)",
+           "unit": "GB/s", "peak": PEAK_HBM_GBPS,
+           "stream_read_gbps": round(nbytes / (ms_stream * 1e-3) / 1e9, 1),
+           "stream_read_frac": round(nbytes / (ms_stream * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+           "tile4k_read_gbps": round(nbytes / (ms_tile * 1e-3) / 1e9, 1),
+           "tile4k_read_frac": round(nbytes / (ms_tile * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+           "config": {"stream": f"1 GiB, {blocks} workgroups of 256 threads, 4 independent 16-byte loads per "
+                                "thread and iteration, 2 buffers alternated",
+                      "tile4k": f"{n_tiles} 4 KiB tiles at random distinct indices of a 4 GiB buffer, {per_wave} "
+                                "tiles per 64-lane wave, 2 index sets alternated",
+                      "timing": f"median of {reps} launches, HIP events"}}
+    log(f"[bench] ceiling: stream {res['stream_read_gbps']} GB/s, 4 KiB tiles {res['tile4k_read_gbps']} GB/s")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama31_8b_gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=4, help="cache copies rotated over steps")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("decode", "prefill", "prefix", "swap", "fp8", "ceiling"), default="decode",
+                    help="print only one measurement")
+    ap.add_argument("--no-extras", "--no-prefill", dest="no_extras", action="store_true",
+                    help="decode line only: leave out the nested objects")
+    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=200,
+                    help="untimed pa_prefill launches before the timed ones (~60 ms: the matrix-core "
+                         "clock takes that long to settle; 10 launches read ~15%% slow)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--compare-contiguous", action="store_true",
+                    help="also time pa_decode_contiguous and identity placement on the chosen workload")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch  # noqa: F401  (CPU work first: nothing below initialises the GPU until the oracle legs are done)
+
+    import workloads as W
+    mode, extras, with_cpu = args.mode, not args.no_extras, not args.no_cpu_baseline
+    key, desc = WORKLOADS[args.workload]
+    wl = wl_ns = wl_pf = None
+    t0 = time.time()
+    if mode in ("decode", "fp8"):
+        wl = W.CONFIGS[key]()
+        if mode == "decode" and extras and args.workload == "llama31_8b_gqa":
+            wl_ns = W.CONFIGS["gqa_noshare"]()
+    if mode == "prefill" or (mode == "decode" and extras):
+        wl_pf = W.llama31_8b_prefill()
+    log(f"[bench] workloads generated in {time.time() - t0:.1f}s")
+    cpu = {}
+    if with_cpu:
+        t0 = time.time()
+        if mode == "decode":
+            cpu["decode"] = cpu_baseline(wl)
+            if wl_ns is not None:
+                cpu["noshare"] = cpu_baseline(wl_ns)
+        if mode == "fp8" or (mode == "decode" and extras):
+            cpu["fp8"] = fp8_cpu_baseline(wl, 1 / 56, 1 / 72)
+        if wl_pf is not None:
+            cpu["prefill"] = prefill_cpu_baseline(wl_pf)
+        log(f"[bench] oracle baselines on {host_cpu()['cores_available']} cores in {time.time() - t0:.1f}s")
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    tail = {"n_gpus": 1, "vs_baseline": None}
+    if mode == "swap":
+        print(json.dumps({**bench_swap(dev, with_cpu), **tail}), flush=True)
+        return
+    if mode == "prefix":
+        print(json.dumps({**bench_prefix(dev, with_cpu), **tail}), flush=True)
+        return
+    if mode == "ceiling":
+        print(json.dumps({**bench_ceiling(dev), **tail}), flush=True)
+        return
+    if mode == "prefill":
+        res = bench_prefill(wl_pf, args.prefill_steps, args.prefill_warmup, dev, cpu.get("prefill"))
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({**res, "scaling": "weak", **tail}), flush=True)
+        return
+    if mode == "fp8":
+        from tests._native import NativeDeviceRun
+        run = NativeDeviceRun(wl, device=dev)
+        res = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas, cpu.get("fp8"),
+                        partition_size=args.partition_size)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({**res, "scaling": "weak", **tail}), flush=True)
+        return
+
+    result, run, dec_avg = bench_decode_step(wl, args.workload, desc, dev, args.steps, args.warmup, args.replicas,
+                                             args.partition_size, cpu.get("decode"))
+    result["n_gpus"] = 1
+    if args.copy_calibration:
+        copy_calibration(dev)
+    if args.compare_contiguous:
+        result["paged_vs_contiguous"] = time_contiguous(wl, run, args.steps, args.replicas, dev,
+                                                        args.partition_size)
+    if extras:
+        if wl_ns is not None:
+            ns, run_ns, _ = bench_decode_step(wl_ns, "llama31_8b_gqa_noshare", WORKLOADS["llama31_8b_gqa_noshare"][1],
+                                              dev, args.steps, args.warmup, args.replicas, args.partition_size,
+                                              cpu.get("noshare"))
+            del run_ns
+            for k in ("metric", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "data"):
+                ns.pop(k, None)
+            result["noshare"] = ns
+            torch.cuda.empty_cache()
         result["fp8"] = bench_fp8(wl, run, args.workload, dev, args.steps, args.warmup, args.replicas,
-                                  not args.no_cpu_baseline, bf16_decode_ms=dec_avg)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on a CPU sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl)
+                                  cpu.get("fp8"), bf16_decode_ms=dec_avg)
+        del run
+        torch.cuda.empty_cache()
+        result["block_sweep"] = bench_block_sweep(dev, max(args.steps, 50), args.replicas)
+        result["ceiling"] = bench_ceiling(dev)
+        result["prefill"] = bench_prefill(wl_pf, args.prefill_steps, args.prefill_warmup, dev, cpu.get("prefill"))
+        result["prefix_cache"] = bench_prefix(dev, with_cpu)
+        result["swap"] = bench_swap(dev, with_cpu)
     print(json.dumps(result), flush=True)
 
 

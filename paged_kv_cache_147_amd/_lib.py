@@ -458,8 +458,9 @@ def _workspace_on(nbytes, device, stream):
     used on ``stream``: when that is another stream, the allocator is told, so
     the memory is not handed out again before the work queued there has run."""
     ws = workspace_for(nbytes, device)
-    if stream is not None and stream.value != torch.cuda.current_stream(device).cuda_stream:
-        ws.record_stream(torch.cuda.ExternalStream(stream.value, device=device))
+    handle = (stream.value or 0) if stream is not None else None     # c_void_p(0).value is None
+    if handle is not None and handle != torch.cuda.current_stream(device).cuda_stream:
+        ws.record_stream(torch.cuda.ExternalStream(handle, device=device))
     return ws
 
 

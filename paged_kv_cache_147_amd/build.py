@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+# Memory-read ceilings for the benchmark: a separate library, not part of the decode path.
+CEILING_LIB = os.path.join(PKG, "libpagedkv_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
@@ -53,23 +56,28 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=True, jobs=None):
-    os.makedirs(OBJDIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
-    with ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, err in results:
-        if err.strip() and verbose:
-            print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-           *[o for o, _ in results]]
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True, jobs=None):
+    os.makedirs(OBJDIR, exist_ok=True)
+    sources = SOURCES + CEILING_SOURCES
+    jobs = jobs or min(len(sources), os.cpu_count() or 4)
+    with ThreadPoolExecutor(jobs) as ex:
+        results = dict(zip(sources, ex.map(_compile, sources)))
+    for _, err in results.values():
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in CEILING_SOURCES], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

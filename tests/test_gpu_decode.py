@@ -334,3 +334,29 @@ except P.PagedKVError as e:
     print(r.stdout[-500:], r.stderr[-500:], flush=True)
     assert r.returncode == 0
     assert "REJECTED True True" in r.stdout          # good call ran; bad call launched nothing
+
+
+def test_workspace_made_by_the_binding_on_any_stream():
+    # with no workspace the binding allocates one; it must work on the default
+    # stream (handle 0) and on another stream (the allocator is told the
+    # memory is in use there)
+    wl = W.independent("ws_streams", [5, 700, 1300], (8, 2, 128, 16, "bf16"), 256, 96, seed=12)
+    dev = NativeDeviceRun(wl)
+    ref = oracle_out(wl)
+    want = dev.decode(partition_size=128)
+    for use_side in (False, True):
+        out = torch.empty_like(want)
+        side = torch.cuda.Stream()
+        if use_side:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                st = P.current_stream()
+            P.pa_decode(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, wl.scale, partition_size=128,
+                        stream=st)
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            P.pa_decode(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, wl.scale, partition_size=128,
+                        stream=P.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), use_side
+        assert_close(out.cpu().numpy(), ref, wl.dtype, f"side stream {use_side}")
