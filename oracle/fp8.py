@@ -83,6 +83,15 @@ def quantize(x, scale):
     return encode(y.astype(np.float32))
 
 
+def quantize_bits16(bits, dtype, scale):
+    """quantize() of 16-bit inputs given as raw bits ("f16" or "bf16"): the
+    codes of all 65536 patterns are computed once with quantize() itself,
+    then looked up, which is the same function over any array of them."""
+    from .bits import to_f64
+    table = quantize(to_f64(np.arange(65536, dtype=np.uint16), dtype).astype(np.float32), scale)
+    return table[np.asarray(bits, dtype=np.uint16)]
+
+
 def dequantize(codes, scale):
     return VALUES[np.asarray(codes, dtype=np.uint8)] * float(np.float32(scale))
 

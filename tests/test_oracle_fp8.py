@@ -117,3 +117,16 @@ def test_planted_mistakes_fail(mutant, monkeypatch):
         monkeypatch.setattr(F, "inv_scale", lambda s: np.float32(1.0))
         with pytest.raises(AssertionError):
             test_quantize_uses_the_float32_reciprocal()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_quantize_bits16_equals_quantize(dtype):
+    # the table path must be quantize() itself: every pattern, and a random array
+    from oracle.bits import to_f64
+    every = np.arange(65536, dtype=np.uint16)
+    for scale in (1 / 56, 0.5, 3.0):
+        assert np.array_equal(F.quantize_bits16(every, dtype, scale),
+                              F.quantize(to_f64(every, dtype).astype(np.float32), scale))
+    bits = np.random.default_rng(3).integers(0, 65536, size=(7, 3, 16, 8), dtype=np.uint16)
+    assert np.array_equal(F.quantize_bits16(bits, dtype, 1 / 72),
+                          F.quantize(to_f64(bits, dtype).astype(np.float32), 1 / 72))
