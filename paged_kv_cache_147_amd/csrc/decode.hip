@@ -713,24 +713,23 @@ void decode_kernel(DecodeParams p) {
   };
 
   if constexpr (!BAL) {
-    const Unit unit = unit_of(blockIdx.x, p);
+    Unit unit;
+    int ctx = 0;
+    const int kind = unit_of(blockIdx.x, p, &unit, &ctx);
+    if (kind == kUnitNone) return;
     g = unit.g;
     s = unit.s;
-    const int part = unit.part;
-    const int ctx = min(p.ctx_lens[s], p.max_ctx);
-    if (ctx <= 0) {
+    if (kind == kUnitZeroRow) {
       // no context: defined as a zero output row
-      if (part == 0) {
-        const int64_t h0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
-        for (int i = lane; i < G * D; i += kWave) {
-          if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[h0 * D + i] = 0.f;
-          else reinterpret_cast<uint16_t*>(p.out)[h0 * D + i] = 0;
-        }
+      const int64_t h0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
+      for (int i = lane; i < G * D; i += kWave) {
+        if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[h0 * D + i] = 0.f;
+        else reinterpret_cast<uint16_t*>(p.out)[h0 * D + i] = 0;
       }
       return;
     }
+    const int part = unit.part;
     const int from = part * p.part_tokens;
-    if (from >= ctx) return;
     const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
     reduce_range(from, min(from + p.part_tokens, ctx));
     finish(nparts_seq == 1, head0 * p.num_parts + part, p.num_parts);
@@ -1006,6 +1005,7 @@ struct Plan {
   bool balanced = false;
   int part_tokens = 0;   // fixed: partition length; balanced: chunk length
   int num_parts = 0;     // fixed only
+  int full_parts = 0;    // fixed only
   int max_ctx = 0;
   int max_pieces = 0;    // balanced: pieces the workspace has room for
   size_t workspace = 0;
@@ -1074,7 +1074,8 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   plan->balanced = false;
   plan->part_tokens = pt;
   plan->num_parts = (ctx_bound + pt - 1) / pt;
-  if (int64_t(plan->num_parts) * (int64_t(S) + kSeqChunk) * Hkv > INT32_MAX)
+  plan->full_parts = ctx_bound / pt;
+  if ((int64_t(plan->full_parts) * padded_seqs(S) + S) * Hkv > INT32_MAX)
     return fail(PA_E_UNSUPPORTED, "too many (partition, sequence, head) units for one launch");
   if (plan->num_parts > 1 && S > 0) {
     const size_t rows = size_t(S) * Hq * plan->num_parts;
@@ -1154,8 +1155,7 @@ template <class T, int D, int G, bool PAGED>
 pa_status launch_group(DecodeParams p, const Plan& plan, int S, int Hkv, hipStream_t st) {
   const dim3 combine_grid(unsigned(int64_t(S) * p.num_q_heads));
   if (!plan.balanced) {
-    const int64_t seqs_padded = (int64_t(S) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
-    launch_decode<T, D, G, PAGED, false>(p, dim3(unsigned(int64_t(p.num_parts) * seqs_padded * Hkv)), st);
+    launch_decode<T, D, G, PAGED, false>(p, dim3(unsigned(grid_units(p))), st);
     pa_status ps = launch_status("decode partition kernel");
     if (ps != PA_OK || p.num_parts <= 1) return ps;
     hipLaunchKernelGGL((decode_combine_kernel<T, D, false>), combine_grid, dim3(kWave), 0, st, p);
@@ -1372,6 +1372,7 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
   p.max_ctx = plan.max_ctx;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
+  p.full_parts = plan.full_parts;
   p.out_f32 = a->out_dtype == PA_F32;
   p.scale_log2e = a->scale * 1.4426950408889634f;
   p.v_scale = 1.f;
@@ -1456,6 +1457,7 @@ extern "C" pa_status pa_decode_contiguous(const pa_contig_args* a, pa_stream str
   p.max_ctx = plan.max_ctx;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
+  p.full_parts = plan.full_parts;
   p.out_f32 = a->out_dtype == PA_F32;
   p.scale_log2e = a->scale * 1.4426950408889634f;
   return launch<false>(p, plan, a->kv_dtype, a->head_dim, a->num_q_heads / a->num_kv_heads, a->num_seqs,

@@ -150,21 +150,20 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
   constexpr int KP = D / 64;  // 16-byte K pieces per lane and row
   constexpr int ROW = D;      // bytes per cached row
   const int lane = threadIdx.x, m16 = lane & 15, q4 = lane >> 4;
-  const Unit unit = unit_of(blockIdx.x, p);
+  Unit unit;
+  int ctx = 0;
+  const int kind = unit_of(blockIdx.x, p, &unit, &ctx);
+  if (kind == kUnitNone) return;
   const int g = unit.g, s = unit.s, part = unit.part;
-  const int ctx = min(p.ctx_lens[s], p.max_ctx);
   const int64_t head0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
-  if (ctx <= 0) {  // no context: defined as a zero output row
-    if (part == 0) {
-      for (int i = lane; i < G * D; i += kWave) {
-        if (p.out_f32) reinterpret_cast<float*>(p.out)[head0 * D + i] = 0.f;
-        else reinterpret_cast<uint16_t*>(p.out)[head0 * D + i] = 0;
-      }
+  if (kind == kUnitZeroRow) {  // no context: defined as a zero output row
+    for (int i = lane; i < G * D; i += kWave) {
+      if (p.out_f32) reinterpret_cast<float*>(p.out)[head0 * D + i] = 0.f;
+      else reinterpret_cast<uint16_t*>(p.out)[head0 * D + i] = 0;
     }
     return;
   }
   const int tok0 = part * p.part_tokens;
-  if (tok0 >= ctx) return;
   const int tok1 = min(tok0 + p.part_tokens, ctx);
   const int nsteps = (tok1 - tok0 + 31) >> 5;
 
@@ -408,8 +407,7 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
 
 template <class T, int D, int G>
 void launch_group(const DecodeParams& p, hipStream_t st) {
-  const int64_t seqs_padded = (int64_t(p.num_seqs) + kSeqChunk - 1) / kSeqChunk * kSeqChunk;
-  const dim3 grid(unsigned(int64_t(p.num_parts) * seqs_padded * p.num_kv_heads));
+  const dim3 grid(unsigned(grid_units(p)));
   if (p.block_size == 8) hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, true>), grid, dim3(kWave), 0, st, p);
   else hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, false>), grid, dim3(kWave), 0, st, p);
 }
