@@ -213,55 +213,33 @@ constexpr int kMinTilesPerPiece = 8;  // fewer pieces than waves when the batch 
 constexpr int kMaxWaves = 8192;       // pieces the workspace is sized for, at most
 
 
-// q.K on the matrix cores: for a GQA group (G >= 2) of 16-bit heads, the
-// scores of 16 tokens x G heads are a small dense contraction over head_dim,
-// done as head_dim / 32 v_mfma_f32_16x16x32 steps (A = 16 K rows, B = the
-// group's queries padded to 16 columns).  MHA (G == 1) and float32 caches use
-// packed dot products on the vector ALUs.
-template <class T, int G>
-constexpr bool mfma_capable() { return T::bytes == 2 && G >= 2; }
+// Scores run on the vector ALUs (v_dot2 on 16-bit pairs) for every group
+// size: 8 lanes share a token row, so each 16-byte load instruction of a wave
+// reads whole 128-byte lines.  The matrix-core form of q.K (A = 16 K rows in
+// the v_mfma_f32_16x16x32 operand layout) reads only 64 bytes of each of 16
+// rows per instruction, twice the L2 requests for the same bytes; measured on
+// MI355X it made the shared-prefix batch (mostly L2 hits) 8% slower and gained
+// at most 2% elsewhere, and decode has arithmetic to spare (removing the
+// score and weighted-sum arithmetic altogether left its time unchanged).
 
-// Score path of a decode_kernel instance.  kScoresMfma reads a 16-token tile
-// as 16 consecutive rows of one block (block_size >= 16, or the contiguous
-// layout) through one scalar resource; kScoresMfmaSplit serves 8-token blocks,
-// where the tile's two halves lie in two blocks and each half of the lanes
-// addresses its own.
-constexpr int kScoresValu = 0;
-constexpr int kScoresMfma = 1;
-constexpr int kScoresMfmaSplit = 2;
-
-// Passes (of 8 token rows) held by one V load buffer; two buffers alternate,
-// so up to 2 * passes_per_buffer * 8 rows are in flight per wave.  The
-// vector-ALU score path uses the same buffers for K.
+// Passes (of 8 token rows) held by one load buffer; two buffers alternate,
+// so up to 2 * passes_per_buffer * 8 rows are in flight per wave, for K and
+// for V.
 template <int G>
 constexpr int passes_per_buffer() { return G <= 2 ? 4 : 2; }
 
 // Rows of LDS scores a partition of `part_tokens` tokens needs: both passes
 // run in pairs of buffers (at most 8 passes = 64 rows per pair), so the count
-// is rounded up to 64 rows; 64 more floats serve as a sink for the MFMA
-// lanes that carry padding heads.
+// is rounded up to 64 rows.
 __host__ __device__ constexpr int lds_rows(int part_tokens) { return (part_tokens + 63) / 64 * 64; }
 template <int G>
-__host__ __device__ constexpr int lds_floats(int part_tokens) { return lds_rows(part_tokens) * G + 64; }
+__host__ __device__ constexpr int lds_floats(int part_tokens) { return lds_rows(part_tokens) * G; }
 // Balanced schedule: chunks of kBalancedChunk tokens, plus G * D floats of
 // running sums.  448 keeps a GQA group of 4 at d = 128 under 10 KB of LDS,
 // so 16 waves fit a CU's 160 KB.
 constexpr int kBalancedChunk = 448;
 template <int G, int D>
 __host__ __device__ constexpr int lds_floats_balanced() { return lds_floats<G>(kBalancedChunk) + G * D; }
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_qk(BF16, uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_qk(F16, uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
 
 // ---- schedules ---------------------------------------------------------------
 //
@@ -308,29 +286,25 @@ __device__ __forceinline__ int piece_of_workgroup(int id, const Sched& sc) {
 
 // 16-bit caches with G <= 4 fit 128 registers, i.e. 4 waves per SIMD (the
 // balanced schedule's loops need the hint to get there without spilling).
-template <class T, int D, int G, bool PAGED, int MFMA, bool BAL>
+template <class T, int D, int G, bool PAGED, bool BAL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(T::bytes == 2 && G <= 4 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
   constexpr int EPC = 16 / T::bytes;          // elements per 16-byte chunk
   constexpr int ROW_BYTES = D * T::bytes;
   constexpr int NCH = ROW_BYTES / 128;        // chunks per lane per row
   constexpr int NV = NCH * EPC;               // values per lane per row (= D / 8)
-  static_assert(!MFMA || mfma_capable<T, G>(), "MFMA scores need 16-bit data and G >= 2");
-  static_assert(MFMA != kScoresMfmaSplit || PAGED, "split tiles serve 8-token blocks");
-  constexpr int U = MFMA ? 2 : passes_per_buffer<G>();
-  constexpr int KT = 1;  // 16-token score tiles per K buffer (MFMA path)
-  constexpr int KK = D / 32;                  // MFMA steps over head_dim
+  constexpr int U = passes_per_buffer<G>();
   static_assert(NCH >= 1, "row must span the 8 lanes");
 
-  extern __shared__ float lds[];  // [rows][G] scores, then weights; + 64-float sink
+  extern __shared__ float lds[];  // [rows][G] scores, then weights (balanced: + running sums)
 
   const int lane_id = threadIdx.x;
-  // Lane coordinates: (r, c) = (lane / 8, lane % 8) for row work, (m, q4) =
-  // (lane % 16, lane / 16) for matrix-core tiles.  They are re-derived at the
-  // start of every chunk and finish (refresh_lane) from an opaque copy of the
-  // lane id, so addresses built from them are not hoisted out of the range
-  // and chunk loops, where they would hold registers across every pass.
-  int lane = lane_id, r = lane >> 3, c = lane & 7, m = lane & 15, q4 = lane >> 4;
+  // Lane coordinates (r, c) = (lane / 8, lane % 8) for row work.  They are
+  // re-derived at the start of every chunk and finish (refresh_lane) from an
+  // opaque copy of the lane id, so addresses built from them are not hoisted
+  // out of the range and chunk loops, where they would hold registers across
+  // every pass.
+  int lane = lane_id, r = lane >> 3, c = lane & 7;
 
   // The range being reduced: sequence s, KV head g, tokens [tok0, tok1) of
   // the current chunk (at most part_tokens of them).
@@ -357,8 +331,6 @@ void decode_kernel(DecodeParams p) {
     lane = l;
     r = l >> 3;
     c = l & 7;
-    m = l & 15;
-    q4 = l >> 4;
     my_h = r * PER / NV;
     e0 = r * PER % NV;
   };
@@ -366,7 +338,7 @@ void decode_kernel(DecodeParams p) {
     const int e = e0 + q;
     return (e / EPC) * (128 / T::bytes) + c * EPC + e % EPC;
   };
-  float* const keep = lds + lds_rows(p.part_tokens) * G + kWave;
+  float* const keep = lds + lds_rows(p.part_tokens) * G;
 
   // First row of pass `pass` (clamped to the last real pass, so padding
   // passes re-read cached rows) and how many of its 8 rows are in the context.
@@ -406,33 +378,17 @@ void decode_kernel(DecodeParams p) {
     }
   };
 
-  // Query registers of the current (s, g).
-  // MFMA: lane (m = lane % 16, q4 = lane / 16) holds, of token m of a
-  // 16-token tile, elements [32 kk + 8 q4, +8) for step kk -- the A layout of
-  // v_mfma_f32_16x16x32 -- and of query head m the same elements as the B
-  // operand (zero for m >= G).  The result D[4 q4 + i][m] is the score of
-  // token 4 q4 + i for head m.
-  // Vector ALU: lane (r, c) holds chunks j * 128 + c * 16 of row r of each
-  // 8-row pass; the query chunks matching them stay in registers.
-  uint4 qb[MFMA ? KK : 1];
-  uint4 qc[MFMA ? 1 : G][NCH];
+  // Query registers of the current (s, g): lane (r, c) holds chunks
+  // j * 128 + c * 16 of row r of each 8-row pass; the query chunks matching
+  // them stay in registers.
+  uint4 qc[G][NCH];
   auto load_q = [&]() {
-    if constexpr (MFMA) {
-      const char* qrow = reinterpret_cast<const char*>(p.q) + (head0 + min(m, G - 1)) * ROW_BYTES + q4 * 16;
-      const uint32_t keep = m < G ? ~0u : 0u;
+    const char* qrow = reinterpret_cast<const char*>(p.q) + head0 * ROW_BYTES + c * 16;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        uint4 v = *reinterpret_cast<const uint4*>(qrow + kk * 64);
-        qb[kk] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-      }
-    } else {
-      const char* qrow = reinterpret_cast<const char*>(p.q) + head0 * ROW_BYTES + c * 16;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < NCH; ++j)
-          qc[h][j] = *reinterpret_cast<const uint4*>(qrow + h * ROW_BYTES + j * 128);
-    }
+      for (int j = 0; j < NCH; ++j)
+        qc[h][j] = *reinterpret_cast<const uint4*>(qrow + h * ROW_BYTES + j * 128);
   };
 
   auto begin_range = [&]() {
@@ -467,141 +423,64 @@ void decode_kernel(DecodeParams p) {
     // ---- pass 1: scores, scaled to the log2 domain, into LDS --------------
     float cmax = -INFINITY;
     uint4 bufA[U][NCH], bufB[U][NCH];
-    if constexpr (MFMA) {
-      // The two 8-row passes of a tile are consecutive rows of one block (or
-      // of the contiguous region), so one resource spans both.
-      auto load_tile = [&](uint4 (&kt)[KK], int tile) {
-        int live0, live1;
-        const char* rows0 = pass_rows(p.k, 2 * tile, live0);
-        const char* rows1 = pass_rows(p.k, 2 * tile + 1, live1);
-        if constexpr (MFMA == kScoresMfmaSplit) {
-          // 8-token blocks: lanes m < 8 read the first pass's block, lanes
-          // m >= 8 the second's (a past-the-end pass is the last one again,
-          // its scores masked), each from its own 64-bit address
-          const bool upper = m >= kRowsPerPass;
-          const int row = min(m & (kRowsPerPass - 1), (upper ? live1 : live0) - 1);
-          const char* rp = (upper ? rows1 : rows0) + row * ROW_BYTES + q4 * 16;
+    auto score_buf = [&](const uint4 (&buf)[U][NCH], int b) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) kt[kk] = *reinterpret_cast<const uint4*>(rp + kk * 64);
-        } else {
-          const int live = 2 * tile + 1 < npass ? kRowsPerPass + live1 : live0;
-          const auto rs = rsrc_of(rows0, 2 * kRowsPerPass);
-          const uint32_t off = uint32_t(min(m, live - 1)) * ROW_BYTES + uint32_t(q4) * 16;
+      for (int u = 0; u < U; ++u) {
+        const int pass = b * U + u;
+        float sc[G];
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) kt[kk] = load16(rs, off + kk * 64);
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, buf[u][j], qc[h][j], a);
+          sc[h] = row8_sum(a);
         }
-      };
-      float* sink = lds + lds_rows(p.part_tokens) * G + lane;
-      auto score_tile = [&](const uint4 (&kt)[KK], int tile) {
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        float mine = sc[0];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk(T{}, kt[kk], qb[kk], sacc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = tile * 16 + q4 * 4 + i;
-          float sc = sacc[i] * p.scale_log2e;
-          if (tok0 + row >= tok1 || m >= G) sc = -INFINITY;  // past the context, or a padding head
-          *(m < G ? lds + row * G + m : sink) = sc;
-          cmax = fmaxf(cmax, sc);
-        }
-      };
-      auto load_tiles = [&](uint4 (&kt)[KT][KK], int b) {
-#pragma unroll
-        for (int t = 0; t < KT; ++t) load_tile(kt[t], b * KT + t);
-      };
-      auto score_tiles = [&](const uint4 (&kt)[KT][KK], int b) {
-#pragma unroll
-        for (int t = 0; t < KT; ++t) score_tile(kt[t], b * KT + t);
-      };
-      const int npairs = (npass + 4 * KT - 1) / (4 * KT);  // pairs of K buffers
-      uint4 ktA[KT][KK], ktB[KT][KK];
-      load_tiles(ktA, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_tiles(ktB, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int i = 0; i < npairs; ++i) {
-        score_tiles(ktA, 2 * i);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tiles(ktA, 2 * i + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        score_tiles(ktB, 2 * i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tiles(ktB, 2 * i + 3);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int h = 1; h < G; ++h) mine = (c % G == h) ? sc[h] : mine;
+        mine *= p.scale_log2e;
+        if (tok0 + pass * kRowsPerPass + r >= tok1) mine = -INFINITY;  // past the context
+        // lanes c and c + G hold the same head: both store the same value
+        lds[(pass * kRowsPerPass + r) * G + c % G] = mine;
+        cmax = fmaxf(cmax, mine);
       }
-      // first V rows start streaming while the weights are formed
-      load_buf(p.v, bufA, 0);
+    };
+    const int npairs = (npass + 2 * U - 1) / (2 * U);
+    load_buf(p.k, bufA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.k, bufB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // The scheduling barriers keep the order "consume one buffer, refill it,
+    // consume the other, refill it", so one buffer is always in flight.
+    for (int i = 0; i < npairs; ++i) {
+      score_buf(bufA, 2 * i);
       __builtin_amdgcn_sched_barrier(0);
-      load_buf(p.v, bufB, 1);
+      load_buf(p.k, bufA, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      // head m's scores sit in lanes m, m+16, m+32, m+48; leave each lane i
-      // with the max of head i % G, as the vector-ALU path does
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      cmax = __shfl(cmax, lane % G);
-    } else {
-      auto score_buf = [&](const uint4 (&buf)[U][NCH], int b) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int pass = b * U + u;
-          float sc[G];
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) a = dot_chunk(T{}, buf[u][j], qc[h][j], a);
-            sc[h] = row8_sum(a);
-          }
-          float mine = sc[0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = (c % G == h) ? sc[h] : mine;
-          mine *= p.scale_log2e;
-          if (tok0 + pass * kRowsPerPass + r >= tok1) mine = -INFINITY;  // past the context
-          // lanes c and c + G hold the same head: both store the same value
-          lds[(pass * kRowsPerPass + r) * G + c % G] = mine;
-          cmax = fmaxf(cmax, mine);
-        }
-      };
-      const int npairs = (npass + 2 * U - 1) / (2 * U);
-      load_buf(p.k, bufA, 0);
+      score_buf(bufB, 2 * i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_buf(p.k, bufB, 1);
+      load_buf(p.k, bufB, 2 * i + 3);
       __builtin_amdgcn_sched_barrier(0);
-      // The scheduling barriers keep the order "consume one buffer, refill it,
-      // consume the other, refill it", so one buffer is always in flight.
-      for (int i = 0; i < npairs; ++i) {
-        score_buf(bufA, 2 * i);
-        __builtin_amdgcn_sched_barrier(0);
-        load_buf(p.k, bufA, 2 * i + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        score_buf(bufB, 2 * i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_buf(p.k, bufB, 2 * i + 3);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // first V rows start streaming while the weights are formed
-      load_buf(p.v, bufA, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_buf(p.v, bufB, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // lane i's cmax belongs to head i % G: reduce over that head's lanes
-#pragma unroll
-      for (int mm = G; mm < kWave; mm <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, mm));
     }
+    // first V rows start streaming while the weights are formed
+    load_buf(p.v, bufA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_buf(p.v, bufB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane i's cmax belongs to head i % G: reduce over that head's lanes
+#pragma unroll
+    for (int mm = G; mm < kWave; mm <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, mm));
 
     // ---- softmax weights against the running max ---------------------------
-    // The V pass runs whole pairs of 2U passes; the score pass wrote whole
-    // pairs of 16-token tiles (MFMA) or the same 2U-pass pairs.  Rows the V
-    // pass reaches beyond the written scores are padding and get weight 0.
+    // Both passes run whole pairs of 2U passes, so every row the V pass
+    // reaches has a score; rows past the context carry -inf and get weight 0.
     const float new_m = fmaxf(run_m, cmax);
     const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
-    const int rows_k = MFMA ? (npass + 4 * KT - 1) / (4 * KT) * (32 * KT) : npass_v * kRowsPerPass;
     __syncthreads();
     float wsum = 0.f;
     const int nent = npass_v * kRowsPerPass * G;
-    const int nent_k = rows_k * G;
     for (int e = lane; e < nent; e += kWave) {  // entry e belongs to head e % G = lane % G
-      const float w = e < nent_k ? __builtin_amdgcn_exp2f(lds[e] - new_m) : 0.f;
+      const float w = __builtin_amdgcn_exp2f(lds[e] - new_m);
       lds[e] = w;
       wsum += w;
     }
@@ -1096,10 +975,10 @@ void bind_workspace(const Plan& plan, void* ws, DecodeParams* p) {
   p->start_seq = reinterpret_cast<int32_t*>(base + plan.start_off);
 }
 
-template <class T, int D, int G, bool PAGED, int MFMA>
+template <class T, int D, int G, bool PAGED>
 int occupancy(size_t lds) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, D, G, PAGED, MFMA, true>, kWave, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, D, G, PAGED, true>, kWave, lds) !=
       hipSuccess)
     return 0;
   return n;
@@ -1107,7 +986,7 @@ int occupancy(size_t lds) {
 
 // Waves of the balanced decode kernel the current GPU holds at once: CUs x
 // resident waves per CU, the smaller over the kernel's variants (paged or
-// contiguous, matrix-core or vector scores) so that all of them cut the work
+// contiguous) so that both cut the work
 // identically; a multiple of 8 in [8, kMaxWaves].  Cached per device.
 std::atomic<int> g_waves_override{0};  // pa_decode_set_waves; 0 = automatic
 
@@ -1125,10 +1004,7 @@ int balanced_waves() {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
   const size_t lds = size_t(lds_floats_balanced<G, D>()) * sizeof(float);
-  int occ = std::min(occupancy<T, D, G, true, kScoresValu>(lds), occupancy<T, D, G, false, kScoresValu>(lds));
-  if constexpr (mfma_capable<T, G>())
-    occ = std::min({occ, occupancy<T, D, G, true, kScoresMfma>(lds), occupancy<T, D, G, false, kScoresMfma>(lds),
-                    occupancy<T, D, G, true, kScoresMfmaSplit>(lds)});
+  const int occ = std::min(occupancy<T, D, G, true>(lds), occupancy<T, D, G, false>(lds));
   if (occ <= 0) return 0;
   const int waves = std::max(8, std::min(kMaxWaves, cus * occ) / 8 * 8);
   cache[dev] = waves;
@@ -1138,17 +1014,7 @@ int balanced_waves() {
 template <class T, int D, int G, bool PAGED, bool BAL>
 void launch_decode(const DecodeParams& p, dim3 grid, hipStream_t st) {
   const size_t lds = size_t(BAL ? lds_floats_balanced<G, D>() : lds_floats<G>(p.part_tokens)) * sizeof(float);
-  if constexpr (mfma_capable<T, G>()) {
-    if constexpr (PAGED) {
-      if (p.block_size < 16) {
-        hipLaunchKernelGGL((decode_kernel<T, D, G, true, kScoresMfmaSplit, BAL>), grid, dim3(kWave), lds, st, p);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, kScoresMfma, BAL>), grid, dim3(kWave), lds, st, p);
-    return;
-  }
-  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, kScoresValu, BAL>), grid, dim3(kWave), lds, st, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, BAL>), grid, dim3(kWave), lds, st, p);
 }
 
 template <class T, int D, int G, bool PAGED>
