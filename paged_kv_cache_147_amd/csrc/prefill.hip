@@ -39,14 +39,17 @@
 //     the LDS tile through ds_read_b64_tr_b16, the gfx950 transposing load
 //     (each 16-lane group reads 4 rows x 16 columns and every lane receives
 //     one column of 4);
-//   * P is split into a 16-bit high part and the 16-bit rounding of the
-//     remainder, two MFMAs per block, so p.V keeps ~16 more bits than a
-//     16-bit P would (a single rounded P alone exceeds the 1e-3 tolerance);
+//   * for a bf16 cache P is split into a bf16 high part and the bf16
+//     rounding of the remainder, two MFMAs per block, so p.V keeps ~16 bits
+//     of P (one bf16 rounding, 8 bits, leaves a relative L2 error near
+//     1e-3); an f16 P, rounded once, keeps 11 bits, which is enough, so an
+//     f16 cache takes one MFMA per block;
 //   * workgroups are issued longest first (the last chunk blocks see the
 //     most keys), so the short ones fill the tail.
 #include "device_common.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -81,18 +84,12 @@ __device__ __forceinline__ f32x4_t mfma(F16, u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  0, 0, 0);
 }
 
-// Two probabilities -> a packed 16-bit high part (round to nearest even) and
-// the packed 16-bit rounding of what the high part leaves out.
+// Two probabilities -> a packed bf16 high part (round to nearest even) and
+// the packed bf16 rounding of what the high part leaves out.
 __device__ __forceinline__ void split(BF16, float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
   const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){ra, rb}, bf16x2_t));
-}
-__device__ __forceinline__ void split(F16, float a, float b, uint32_t& hi, uint32_t& lo) {
-  const f16x2_t h = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const f32x2_t hw = __builtin_convertvector(h, f32x2_t);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - hw.x, b - hw.y}, f16x2_t));
 }
 
 // Max / sum with the lane 16 or 32 positions away: after a permlane swap of
@@ -200,6 +197,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int TPB = TPW * kWaves;       // chunk tokens per workgroup
   static_assert(TILE % (kThreads * 16) == 0, "a step's tile must split into whole wave loads");
   static_assert(kStages == 4, "steps go in pairs: two stages computed while two fill");
+
+  // bf16 probabilities go in as two 16-bit parts, f16 ones as one
+  constexpr bool kSplit = std::is_same<T, BF16>::value;
 
   __shared__ __align__(16) char lds[kStages][2][TILE];   // [stage][K, V][32 rows]
 
@@ -451,10 +451,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       // 16 + 4 q4 + e - 4 (e >= 4), i.e. exactly pr[e].
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        uint32_t hi, lo;
-        split(T{}, pr[2 * e], pr[2 * e + 1], hi, lo);
-        PH[j][e] = hi;
-        PL[j][e] = lo;
+        if constexpr (kSplit) {
+          uint32_t hi, lo;
+          split(T{}, pr[2 * e], pr[2 * e + 1], hi, lo);
+          PH[j][e] = hi;
+          PL[j][e] = lo;
+        } else {
+          PH[j][e] = pack2(T{}, pr[2 * e], pr[2 * e + 1]);
+        }
       }
     }
 #pragma unroll
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int j = 0; j < kSub; ++j) {
         o[j][nn] = mfma(T{}, va, PH[j], o[j][nn]);
-        o[j][nn] = mfma(T{}, va, PL[j], o[j][nn]);
+        if constexpr (kSplit) o[j][nn] = mfma(T{}, va, PL[j], o[j][nn]);
       }
     }
   };
