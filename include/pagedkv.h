@@ -316,21 +316,12 @@ pa_status pa_swap_in(void* k_cache, void* v_cache, const int32_t* blocks, int32_
  * weighted sum of V; the attention itself is unchanged).  The new token must
  * have been written already (it attends to itself).
  *
- * Contexts are cut into pieces that are reduced independently and merged
- * with the log-sum-exp identity (which needs the workspace).  Two ways of
- * cutting them (partition_size):
- *   >= 0 fixed partitions, one wave each, as on the pages (vLLM's
- *        partitioned kernel): a sequence's result depends only on its own
- *        inputs.  0 picks the length automatically (512, 256 or 128 tokens:
- *        the largest giving >= 2048 sequence x KV head x partition units).
- *   -1   balanced: the (KV head, sequence) token ranges of the whole batch,
- *        laid end to end in 16-token tiles, are cut into equal pieces, one
- *        per wave the GPU holds at once, so every compute unit streams the
- *        same number of bytes.  The cut depends on all context lengths of
- *        the batch and on the GPU's wave count (see pa_decode_set_waves).
- *        A few per cent faster on batches of private contexts; much slower
- *        when sequences share blocks (forks, beams), which the fixed grid
- *        reads for all sharers at once.
+ * Contexts are cut into fixed partitions of partition_size tokens, one wave
+ * each, as on the pages (vLLM's partitioned kernel), reduced independently
+ * and merged with the log-sum-exp identity (which needs the workspace); a
+ * sequence's result depends only on its own inputs.  partition_size 0 picks
+ * the length automatically (512, 256 or 128 tokens: the largest giving
+ * >= 2048 sequence x KV head x partition units).
  * Arithmetic is float32 (16-bit inputs are widened exactly); results do not
  * depend on which physical blocks hold the tokens, and are bitwise
  * reproducible for the same inputs on the same GPU with the same
@@ -356,10 +347,10 @@ typedef struct pa_decode_args {
   int32_t max_ctx;             /* 0 or an upper bound on ctx_lens; sizes the grid
                                   (0 means max_blocks * block_size) */
   float scale;                 /* finite, e.g. 1/sqrt(head_dim) */
-  int32_t partition_size;      /* 0 = automatic fixed partitions, -1 = balanced
-                                  schedule, else fixed partitions of that many
+  int32_t partition_size;      /* 0 = automatic, else partitions of that many
                                   tokens: a multiple of 8 and of block_size, at
-                                  most min(512, 64 * block_size) */
+                                  most min(512, 64 * block_size) (PA_E_INVAL
+                                  otherwise, negative values included) */
   void* workspace;             /* device scratch, >= pa_decode_workspace_bytes,
                                   256-byte aligned */
   size_t workspace_bytes;
@@ -372,8 +363,7 @@ typedef struct pa_decode_args {
   float v_scale;               /* finite, > 0 */
 } pa_decode_args;
 /*
- * E4M3 caches: fixed partitions only (partition_size >= 0).
- * Codes are widened exactly to q_dtype, q.K and p.V run on the matrix cores
+ * E4M3 caches: codes are widened exactly to q_dtype, q.K and p.V run on the matrix cores
  * with float32 accumulation (p as a 16-bit value plus the 16-bit rounding of
  * its remainder), k_scale is folded into the score scale and v_scale into
  * the weighted sums.
@@ -509,15 +499,6 @@ typedef struct pa_contig_args {
 pa_status pa_decode_contiguous_workspace_bytes(const pa_contig_args* args, size_t* bytes_out);
 pa_status pa_decode_contiguous(const pa_contig_args* args, pa_stream stream);
 
-/*
- * Waves the balanced schedule cuts the work into, for this process: 0 =
- * automatic (compute units x waves of the decode kernel one compute unit
- * holds, which keeps every CU streaming to the end), else rounded down to a
- * multiple of 8 in [8, 8192].  Fewer waves leave room for other kernels
- * running at the same time.  Takes effect for calls made after it; returns
- * the previous setting.
- */
-int pa_decode_set_waves(int32_t waves);
 
 #ifdef __cplusplus
 }

@@ -121,7 +121,6 @@ _SIGS = {
     "pa_decode_static": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp]),
     "pa_decode_contiguous_workspace_bytes": (c_i32, [ctypes.POINTER(pa_contig_args), ctypes.POINTER(c_sz)]),
     "pa_decode_contiguous": (c_i32, [ctypes.POINTER(pa_contig_args), c_vp]),
-    "pa_decode_set_waves": (c_i32, [c_i32]),
     "pa_decode_validate": (c_i32, [ctypes.POINTER(pa_decode_args), c_vp, c_vp]),
     "pa_prefill": (c_i32, [ctypes.POINTER(pa_prefill_args), c_vp]),
 }
@@ -551,12 +550,6 @@ def pa_decode_contiguous(out, q, k, v, ctx_lens, scale, max_ctx=0, partition_siz
     check(_lib.pa_decode_contiguous(ctypes.byref(a), stream if stream is not None else current_stream()),
           "pa_decode_contiguous")
     return workspace
-
-
-def pa_decode_set_waves(waves):
-    """Waves the balanced schedule cuts the work into (0 = automatic); returns
-    the previous setting."""
-    return int(_lib.pa_decode_set_waves(int(waves)))
 
 
 def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, stream=None):

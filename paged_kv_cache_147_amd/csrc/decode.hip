@@ -39,7 +39,6 @@
 #include "device_common.h"
 
 #include <algorithm>
-#include <atomic>
 #include <cstdlib>
 #include <string>
 #include <cmath>
@@ -64,7 +63,6 @@ constexpr int kMaxPartition = 512;
 // partitions amortise each wave's fixed costs; enough units keep every CU
 // busy.
 constexpr int64_t kAutoMinUnits = 2048;
-constexpr int kBalanced = -1;  // partition_size value selecting the balanced schedule
 
 // ---- element helpers ------------------------------------------------------
 
@@ -208,9 +206,6 @@ __device__ __forceinline__ void store_run(T, uint16_t* o, const float* a, float 
 
 // ---- kernels ----------------------------------------------------------------
 
-constexpr int kTile = 16;             // tokens per schedule tile
-constexpr int kMinTilesPerPiece = 8;  // fewer pieces than waves when the batch is small
-constexpr int kMaxWaves = 8192;       // pieces the workspace is sized for, at most
 
 
 // Scores run on the vector ALUs (v_dot2 on 16-bit pairs) for every group
@@ -234,59 +229,15 @@ constexpr int passes_per_buffer() { return G <= 2 ? 4 : 2; }
 __host__ __device__ constexpr int lds_rows(int part_tokens) { return (part_tokens + 63) / 64 * 64; }
 template <int G>
 __host__ __device__ constexpr int lds_floats(int part_tokens) { return lds_rows(part_tokens) * G; }
-// Balanced schedule: chunks of kBalancedChunk tokens, plus G * D floats of
-// running sums.  448 keeps a GQA group of 4 at d = 128 under 10 KB of LDS,
-// so 16 waves fit a CU's 160 KB.
-constexpr int kBalancedChunk = 448;
-template <int G, int D>
-__host__ __device__ constexpr int lds_floats_balanced() { return lds_floats<G>(kBalancedChunk) + G * D; }
 
-// ---- schedules ---------------------------------------------------------------
+// ---- schedule ------------------------------------------------------------------
 //
-// Fixed partitions (partition_size >= 0, the default): one wave per
-// (partition, KV head, sequence), partition = a fixed number of tokens, as on
-// the pages; the hardware dispatcher hands units to CUs as slots free up.
-//
-// Balanced (partition_size == -1): the (KV head, sequence) token ranges are
-// laid end to end in 16-token tiles, KV head major, and cut into as many equal
-// contiguous pieces as the GPU holds waves at once; each wave streams one
-// piece, so every CU is handed the same bytes.  A wave's piece covers whole
-// sequences (finished and written directly) and at most two cut ones (its
-// first and its last); a cut sequence leaves one (max, sum, weighted sum)
-// record per piece, merged by the combine kernel in token order.
-// Measured on MI355X it gains a few per cent on batches with private
-// contexts and loses heavily when sequences share blocks: equal pieces start
-// at unrelated token offsets, so sequences that share a prefix read it at
-// different times and miss in L2, where the fixed grid reads it for all of
-// them at once.  It is also limited by the order in which a SIMD serves its
-// waves: the oldest wave issues first, so of four equal pieces on one SIMD
-// the first finishes in about half the time of the last.
+// Fixed partitions: one wave per (partition, KV head, sequence), partition =
+// a fixed number of tokens, as on the pages; the hardware dispatcher hands
+// units to CUs as slots free up (grid order: unit_of).
 
-
-// Piece k of the balanced schedule covers flattened tiles
-// [piece_start(k), piece_start(k + 1)); piece_of(pos) is the piece holding
-// tile pos.  Both are exact integer formulas, so every kernel agrees on them.
-__device__ __forceinline__ int64_t piece_start(int64_t k, const Sched& sc) {
-  return k * sc.total / sc.pieces;
-}
-__device__ __forceinline__ int64_t piece_of(int64_t pos, const Sched& sc) {
-  return ((pos + 1) * sc.pieces - 1) / sc.total;
-}
-
-// Workgroup id -> piece.  Workgroups are dealt to the 8 XCDs in turn, so XCD x
-// runs ids x, x + 8, ...; giving it pieces [x * per, (x + 1) * per) keeps one
-// contiguous eighth of the tile order -- the same KV heads, neighbouring
-// sequences -- on one XCD's L2.  Returns -1 for an idle workgroup.
-__device__ __forceinline__ int piece_of_workgroup(int id, const Sched& sc) {
-  const int per = (sc.pieces + 7) / 8;
-  const int j = id / 8;
-  const int k = (id % 8) * per + j;
-  return (j < per && k < sc.pieces) ? k : -1;
-}
-
-// 16-bit caches with G <= 4 fit 128 registers, i.e. 4 waves per SIMD (the
-// balanced schedule's loops need the hint to get there without spilling).
-template <class T, int D, int G, bool PAGED, bool BAL>
+// 16-bit caches with G <= 4 fit 128 registers, i.e. 4 waves per SIMD.
+template <class T, int D, int G, bool PAGED>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(T::bytes == 2 && G <= 4 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
   constexpr int EPC = 16 / T::bytes;          // elements per 16-byte chunk
@@ -296,28 +247,25 @@ void decode_kernel(DecodeParams p) {
   constexpr int U = passes_per_buffer<G>();
   static_assert(NCH >= 1, "row must span the 8 lanes");
 
-  extern __shared__ float lds[];  // [rows][G] scores, then weights (balanced: + running sums)
+  extern __shared__ float lds[];  // [rows][G] scores, then weights
 
   const int lane_id = threadIdx.x;
   // Lane coordinates (r, c) = (lane / 8, lane % 8) for row work.  They are
-  // re-derived at the start of every chunk and finish (refresh_lane) from an
-  // opaque copy of the lane id, so addresses built from them are not hoisted
-  // out of the range and chunk loops, where they would hold registers across
-  // every pass.
+  // re-derived at the start of the partition's passes and at its finish
+  // (refresh_lane) from an opaque copy of the lane id, so addresses built
+  // from them are not hoisted to the top of the kernel, where they would hold
+  // registers across every pass.
   int lane = lane_id, r = lane >> 3, c = lane & 7;
 
-  // The range being reduced: sequence s, KV head g, tokens [tok0, tok1) of
-  // the current chunk (at most part_tokens of them).
+  // The partition being reduced: sequence s, KV head g, tokens [tok0, tok1)
+  // (at most part_tokens of them).
   int s = 0, g = 0, tok0 = 0, tok1 = 0, npass = 0;
   int64_t head0 = 0;  // first query row of (s, g)
   int lane_block = 0;
 
-  // Running state over the chunks of a range: lane i keeps, for head i % G,
-  // the running max and weight sum.  acc holds each lane's rows' share of the
-  // current chunk's weighted V sums; with the balanced schedule a range may
-  // take several chunks, and the running sums of the earlier ones wait in
-  // LDS (head h at keep + h * D).
-  float acc[G * NV];  // [head][value]; after a chunk's reduction, PER sums per lane
+  // Lane i keeps, for head i % G, the partition's max and weight sum; acc
+  // holds each lane's rows' share of the weighted V sums.
+  float acc[G * NV];  // [head][value]; after the reduction, PER sums per lane
   float run_m = -INFINITY, run_l = 0.f;
   // After the reduction lane (r, c) holds sums [r PER, (r + 1) PER) of the
   // flattened (head, value) index: head my_h, values e0 .. e0 + PER - 1 at
@@ -338,7 +286,6 @@ void decode_kernel(DecodeParams p) {
     const int e = e0 + q;
     return (e / EPC) * (128 / T::bytes) + c * EPC + e % EPC;
   };
-  float* const keep = lds + lds_rows(p.part_tokens) * G;
 
   // First row of pass `pass` (clamped to the last real pass, so padding
   // passes re-read cached rows) and how many of its 8 rows are in the context.
@@ -397,17 +344,16 @@ void decode_kernel(DecodeParams p) {
     run_l = 0.f;
   };
 
-  // Reduces tokens [tok0, tok1) into the running state; `first` and `last`
-  // say where the chunk sits in its range.
-  auto chunk = [&](bool first, bool last) {
+  // Reduces tokens [tok0, tok1) into run_m, run_l and acc.
+  auto reduce = [&]() {
     refresh_lane();
     npass = (tok1 - tok0 + kRowsPerPass - 1) / kRowsPerPass;
-    // Per chunk, so the query registers are free during the V pass; the
-    // compiler barrier keeps the loads (invariant over a range) from being
-    // hoisted out of the chunk loop, which would pin them through it.
+    // Here, so the query registers are free during the V pass; the compiler
+    // barrier keeps the loads from being hoisted to the top of the kernel,
+    // which would pin them through the K pass set-up.
     asm volatile("" ::: "memory");
     load_q();
-    // Physical ids of this chunk's blocks, one per lane (clamped into the
+    // Physical ids of the partition's blocks, one per lane (clamped into the
     // pool so a corrupt table cannot read outside the caches).
     if constexpr (PAGED) {
       const int b0 = tok0 >> p.log2_block;
@@ -418,7 +364,6 @@ void decode_kernel(DecodeParams p) {
         lane_block = min(max(id, 0), p.num_blocks - 1);
       }
     }
-    __syncthreads();  // the previous chunk's weights have all been read
 
     // ---- pass 1: scores, scaled to the log2 domain, into LDS --------------
     float cmax = -INFINITY;
@@ -471,10 +416,10 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int mm = G; mm < kWave; mm <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, mm));
 
-    // ---- softmax weights against the running max ---------------------------
+    // ---- softmax weights against the partition's max --------------------------
     // Both passes run whole pairs of 2U passes, so every row the V pass
     // reaches has a score; rows past the context carry -inf and get weight 0.
-    const float new_m = fmaxf(run_m, cmax);
+    const float new_m = cmax;
     const int npass_v = (npass + 2 * U - 1) / (2 * U) * (2 * U);
     __syncthreads();
     float wsum = 0.f;
@@ -486,10 +431,7 @@ void decode_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int mm = G; mm < kWave; mm <<= 1) wsum += __shfl_xor(wsum, mm);
-    // Earlier chunks were weighted against run_m: their sums scale by f
-    // (0 on the first chunk, whose running sum is 0).
-    const float f = __builtin_amdgcn_exp2f(run_m - new_m);
-    run_l = run_l * f + wsum;
+    run_l = wsum;
     run_m = new_m;
     __syncthreads();
 
@@ -528,39 +470,9 @@ void decode_kernel(DecodeParams p) {
     }
 
     reduce_scatter8(acc, lane);
-
-    // Several chunks: the running sums of the earlier ones wait in LDS,
-    // head h's at keep + h * D (every lane its own words).
-    if constexpr (BAL) {
-      if (!first) {
-        const float fh = __shfl(f, my_h);  // lane h holds head h's factor
-#pragma unroll
-        for (int q = 0; q < PER; ++q) acc[q] = fmaf(keep[my_h * D + elem(q)], fh, acc[q]);
-      }
-      if (!last) {
-#pragma unroll
-        for (int q = 0; q < PER; q += RUN) store_run<RUN>(keep + my_h * D + elem(q), acc + q, 1.f);
-      }
-    }
   };
 
-  // Reduces tokens [from, to) of (s, g) chunk by chunk.
-  auto reduce_range = [&](int from, int to) {
-    begin_range();
-    if constexpr (!BAL) {  // a partition is one chunk
-      tok0 = from;
-      tok1 = to;
-      chunk(true, true);
-    } else {
-      for (int t = from; t < to; t += p.part_tokens) {
-        tok0 = t;
-        tok1 = min(t + p.part_tokens, to);
-        chunk(t == from, tok1 == to);
-      }
-    }
-  };
-
-  // Finishes the range: the group's normalised output rows when the range is
+  // Finishes the partition: the group's normalised output rows when it is
   // the whole context, else one (max, sum, weighted sum) record per head at
   // rows rec0 + h * rec_stride of the workspace.
   auto finish = [&](bool whole, int64_t rec0, int64_t rec_stride) {
@@ -591,116 +503,29 @@ void decode_kernel(DecodeParams p) {
     }
   };
 
-  if constexpr (!BAL) {
-    Unit unit;
-    int ctx = 0;
-    const int kind = unit_of(blockIdx.x, p, &unit, &ctx);
-    if (kind == kUnitNone) return;
-    g = unit.g;
-    s = unit.s;
-    if (kind == kUnitZeroRow) {
-      // no context: defined as a zero output row
-      const int64_t h0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
-      for (int i = lane; i < G * D; i += kWave) {
-        if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[h0 * D + i] = 0.f;
-        else reinterpret_cast<uint16_t*>(p.out)[h0 * D + i] = 0;
-      }
-      return;
+  Unit unit;
+  int ctx = 0;
+  const int kind = unit_of(blockIdx.x, p, &unit, &ctx);
+  if (kind == kUnitNone) return;
+  g = unit.g;
+  s = unit.s;
+  if (kind == kUnitZeroRow) {
+    // no context: defined as a zero output row
+    const int64_t h0 = int64_t(s) * p.num_q_heads + int64_t(g) * G;
+    for (int i = lane; i < G * D; i += kWave) {
+      if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[h0 * D + i] = 0.f;
+      else reinterpret_cast<uint16_t*>(p.out)[h0 * D + i] = 0;
     }
-    const int part = unit.part;
-    const int from = part * p.part_tokens;
-    const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
-    reduce_range(from, min(from + p.part_tokens, ctx));
-    finish(nparts_seq == 1, head0 * p.num_parts + part, p.num_parts);
-  } else {
-    const Sched sc = *p.sched;
-    const int k = piece_of_workgroup(blockIdx.x, sc);
-    if (k < 0) return;
-    const int64_t first = piece_start(k, sc);
-    const int64_t end = piece_start(k + 1, sc);
-    int64_t pos = first;
-    g = int(pos / sc.tiles_per_head);
-    s = p.start_seq[k];
-    for (;;) {
-      const int c0 = p.cum[s];
-      const int n = p.cum[s + 1] - c0;
-      const int64_t seg = int64_t(g) * sc.tiles_per_head + c0;  // first tile of (s, g)
-      const int t0 = int(pos - seg);
-      const int t1 = int(min(end - seg, int64_t(n)));
-      const int ctx = min(p.ctx_lens[s], p.max_ctx);
-      reduce_range(t0 * kTile, min(t1 * kTile, ctx));
-      // A cut range is this piece's first (it holds piece_start(k)) or its last.
-      const int64_t slot = 2 * int64_t(k) + (pos == first ? 0 : 1);
-      finish(t0 == 0 && t1 == n, slot * G, 1);
-      pos = seg + t1;
-      if (pos >= end) break;
-      do {  // next sequence with a context (one exists: pos < end <= total)
-        if (++s == p.num_seqs) {
-          s = 0;
-          ++g;
-        }
-      } while (p.cum[s + 1] == p.cum[s]);
-    }
+    return;
   }
-}
-
-// Builds the balanced schedule in the workspace: cum[s] = tiles of sequences
-// before s (per KV head), the header, and start_seq[k] = the sequence that
-// holds piece k's first tile.  One workgroup.
-constexpr int kPlanThreads = 1024;
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams p) {
-  __shared__ int wave_sums[kPlanThreads / kWave];
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
-  const int S = p.num_seqs;
-  int carry = 0;
-  for (int base = 0; base < S; base += kPlanThreads) {
-    const int s = base + tid;
-    int n = 0;
-    if (s < S) {
-      const int ctx = min(p.ctx_lens[s], p.max_ctx);
-      n = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
-    }
-    int x = n;  // inclusive scan over the workgroup
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) wave_sums[wave] = x;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < kPlanThreads / kWave; ++w) {
-      before += w < wave ? wave_sums[w] : 0;
-      total += wave_sums[w];
-    }
-    if (s < S) p.cum[s] = carry + before + x - n;
-    carry += total;
-    __syncthreads();  // wave_sums is reused
-  }
-  const int T = carry;
-  Sched sc;
-  sc.tiles_per_head = T;
-  sc.total = int64_t(p.num_kv_heads) * T;
-  sc.pieces = int(min(int64_t(p.num_waves), sc.total / kMinTilesPerPiece));
-  if (sc.total > 0 && sc.pieces == 0) sc.pieces = 1;
-  if (tid == 0) {
-    p.cum[S] = T;
-    *p.sched = sc;
-  }
-  __syncthreads();  // cum complete
-  if (sc.pieces == 0) return;
-  // Pieces whose first tile lies in (s, g): k in [piece_of(A - 1) + 1, piece_of(B - 1)].
-  const int64_t nseg = int64_t(p.num_kv_heads) * S;
-  for (int64_t idx = tid; idx < nseg; idx += kPlanThreads) {
-    const int g = int(idx / S), s = int(idx % S);
-    const int c0 = p.cum[s], c1 = p.cum[s + 1];
-    if (c1 == c0) continue;
-    const int64_t A = int64_t(g) * T + c0, B = int64_t(g) * T + c1;
-    const int64_t k0 = A == 0 ? 0 : piece_of(A - 1, sc) + 1;
-    const int64_t k1 = piece_of(B - 1, sc);
-    for (int64_t k = k0; k <= k1; ++k) p.start_seq[k] = s;
-  }
+  const int part = unit.part;
+  const int from = part * p.part_tokens;
+  const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
+  begin_range();
+  tok0 = from;
+  tok1 = min(from + p.part_tokens, ctx);
+  reduce();
+  finish(nparts_seq == 1, head0 * p.num_parts + part, p.num_parts);
 }
 
 // Merges the records of each (sequence, query head):
@@ -712,11 +537,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams 
 // Every load address is known up front: with at most 64 records (the usual
 // case) the (m, l) loads and the first 8 records' outputs are in flight
 // together, so the merge waits on memory about once after the context length.
-//   fixed partitions: record i = partition i, rows (head * num_parts + i);
-//   balanced: the pieces k_lo..k_hi that cut the range, row (slot * G + h)
-//   with slot 2 k_lo + (range starts inside piece k_lo), then 2 k; a range
-//   inside one piece was written whole, and an empty context gives zeros.
-template <class T, int D, bool BAL>
+// Record i = partition i, row (head * num_parts + i).
+template <class T, int D>
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   const int64_t head = blockIdx.x;  // s * Hq + query head
   const int s = int(head / p.num_q_heads);
@@ -724,39 +546,11 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   const int ctx = min(p.ctx_lens[s], p.max_ctx);
   constexpr int PER = D / kWave;  // output values per lane
   const int64_t obase = head * D + lane * PER;
-  int np;
-  int64_t rec0 = 0, stride = 1, first_rec = 0;
-  if constexpr (!BAL) {
-    if (ctx <= 0) return;  // the partition kernel wrote the zero row
-    np = (ctx + p.part_tokens - 1) / p.part_tokens;
-    if (np <= 1) return;  // the partition kernel wrote this output itself
-    rec0 = first_rec = head * p.num_parts;
-    stride = 1;
-  } else {
-    if (ctx <= 0) {
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        if (p.out_f32 || T::bytes == 4) reinterpret_cast<float*>(p.out)[obase + k] = 0.f;
-        else reinterpret_cast<uint16_t*>(p.out)[obase + k] = 0;
-      }
-      return;
-    }
-    const Sched sc = *p.sched;
-    const int G = p.num_q_heads / p.num_kv_heads;
-    const int qh = int(head % p.num_q_heads);
-    const int g = qh / G, hl = qh % G;
-    const int c0 = p.cum[s], c1 = p.cum[s + 1];
-    const int64_t A = int64_t(g) * sc.tiles_per_head + c0;
-    const int64_t B = int64_t(g) * sc.tiles_per_head + c1;
-    const int64_t klo = piece_of(A, sc), khi = piece_of(B - 1, sc);
-    if (klo == khi) return;  // written whole by the decode kernel
-    np = int(khi - klo + 1);
-    // record i (i >= 1) sits at slot 2 (klo + i): rows (2 (klo + i)) G + hl
-    rec0 = 2 * klo * G + hl;
-    stride = 2 * G;
-    first_rec = (2 * klo + (A == piece_start(klo, sc) ? 0 : 1)) * G + hl;
-  }
-  auto rec = [&](int i) -> int64_t { return i == 0 ? first_rec : rec0 + int64_t(i) * stride; };
+  if (ctx <= 0) return;  // the partition kernel wrote the zero row
+  const int np = (ctx + p.part_tokens - 1) / p.part_tokens;
+  if (np <= 1) return;  // the partition kernel wrote this output itself
+  const int64_t rec0 = head * p.num_parts;
+  auto rec = [&](int i) -> int64_t { return rec0 + i; };
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml);
   const float* po = p.part_o + lane * PER;
 
@@ -881,14 +675,12 @@ int log2_exact(int x) {
 }
 
 struct Plan {
-  bool balanced = false;
-  int part_tokens = 0;   // fixed: partition length; balanced: chunk length
-  int num_parts = 0;     // fixed only
-  int full_parts = 0;    // fixed only
+  int part_tokens = 0;   // partition length
+  int num_parts = 0;     // partitions of the longest context
+  int full_parts = 0;    // partitions that can be full under the bound
   int max_ctx = 0;
-  int max_pieces = 0;    // balanced: pieces the workspace has room for
   size_t workspace = 0;
-  size_t part_o_off = 0, part_ml_off = 0, sched_off = 0, cum_off = 0, start_off = 0;
+  size_t part_o_off = 0, part_ml_off = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -909,31 +701,6 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
   if (int64_t(S) * Hq > INT32_MAX) return fail(PA_E_UNSUPPORTED, "too many (sequence, head) rows");
   plan->max_ctx = ctx_bound;
   plan->workspace = 0;
-  if (partition == kBalanced) {
-    // Balanced schedule; chunks of kBalancedChunk tokens (a multiple of 16,
-    // so of every block size up to 16, and at most 64 blocks of 8 tokens).
-    plan->balanced = true;
-    plan->part_tokens = kBalancedChunk;
-    const int64_t tiles = (int64_t(ctx_bound) + kTile - 1) / kTile;
-    if (int64_t(S) * tiles > INT32_MAX) return fail(PA_E_UNSUPPORTED, "num_seqs * max_ctx too large");
-    const int64_t bound = int64_t(S) * Hkv * tiles / kMinTilesPerPiece;
-    plan->max_pieces = int(std::max<int64_t>(1, std::min<int64_t>(bound, kMaxWaves)));
-    if (S == 0) return ok();
-    size_t off = 0;
-    plan->sched_off = off;
-    off += align256(sizeof(Sched));
-    plan->cum_off = off;
-    off += align256(size_t(S + 1) * sizeof(int32_t));
-    plan->start_off = off;
-    off += align256(size_t(plan->max_pieces) * sizeof(int32_t));
-    const size_t recs = size_t(2) * plan->max_pieces * G;  // two records per piece and head
-    plan->part_ml_off = off;
-    off += align256(recs * 2 * sizeof(float));
-    plan->part_o_off = off;
-    off += align256(recs * D * sizeof(float));
-    plan->workspace = off;
-    return ok();
-  }
   const int unit = block > 8 ? block : 8;
   const int cap = block > 0 ? (64 * block < kMaxPartition ? 64 * block : kMaxPartition) : kMaxPartition;
   int pt = partition;
@@ -948,9 +715,8 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
     }
   }
   if (pt <= 0 || pt % unit || pt > cap)
-    return fail(PA_E_INVAL, "partition_size must be a multiple of 8 and of block_size, at most " +
+    return fail(PA_E_INVAL, "partition_size must be 0 or a multiple of 8 and of block_size, at most " +
                                 std::to_string(cap));
-  plan->balanced = false;
   plan->part_tokens = pt;
   plan->num_parts = (ctx_bound + pt - 1) / pt;
   plan->full_parts = ctx_bound / pt;
@@ -970,73 +736,21 @@ void bind_workspace(const Plan& plan, void* ws, DecodeParams* p) {
   char* base = static_cast<char*>(ws);
   p->part_o = reinterpret_cast<float*>(base + plan.part_o_off);
   p->part_ml = reinterpret_cast<float*>(base + plan.part_ml_off);
-  p->sched = reinterpret_cast<Sched*>(base + plan.sched_off);
-  p->cum = reinterpret_cast<int32_t*>(base + plan.cum_off);
-  p->start_seq = reinterpret_cast<int32_t*>(base + plan.start_off);
 }
 
 template <class T, int D, int G, bool PAGED>
-int occupancy(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, D, G, PAGED, true>, kWave, lds) !=
-      hipSuccess)
-    return 0;
-  return n;
-}
-
-// Waves of the balanced decode kernel the current GPU holds at once: CUs x
-// resident waves per CU, the smaller over the kernel's variants (paged or
-// contiguous) so that both cut the work
-// identically; a multiple of 8 in [8, kMaxWaves].  Cached per device.
-std::atomic<int> g_waves_override{0};  // pa_decode_set_waves; 0 = automatic
-
-template <class T, int D, int G>
-int balanced_waves() {
-  const int forced = g_waves_override.load(std::memory_order_relaxed);
-  if (forced > 0) return forced;
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  const size_t lds = size_t(lds_floats_balanced<G, D>()) * sizeof(float);
-  const int occ = std::min(occupancy<T, D, G, true>(lds), occupancy<T, D, G, false>(lds));
-  if (occ <= 0) return 0;
-  const int waves = std::max(8, std::min(kMaxWaves, cus * occ) / 8 * 8);
-  cache[dev] = waves;
-  return waves;
-}
-
-template <class T, int D, int G, bool PAGED, bool BAL>
 void launch_decode(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  const size_t lds = size_t(BAL ? lds_floats_balanced<G, D>() : lds_floats<G>(p.part_tokens)) * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED, BAL>), grid, dim3(kWave), lds, st, p);
+  const size_t lds = size_t(lds_floats<G>(p.part_tokens)) * sizeof(float);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, PAGED>), grid, dim3(kWave), lds, st, p);
 }
 
 template <class T, int D, int G, bool PAGED>
 pa_status launch_group(DecodeParams p, const Plan& plan, int S, int Hkv, hipStream_t st) {
   const dim3 combine_grid(unsigned(int64_t(S) * p.num_q_heads));
-  if (!plan.balanced) {
-    launch_decode<T, D, G, PAGED, false>(p, dim3(unsigned(grid_units(p))), st);
-    pa_status ps = launch_status("decode partition kernel");
-    if (ps != PA_OK || p.num_parts <= 1) return ps;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, false>), combine_grid, dim3(kWave), 0, st, p);
-    return launch_status("decode combine kernel");
-  }
-  const int waves = balanced_waves<T, D, G>();
-  if (waves <= 0) return fail(PA_E_HIP, "could not size the balanced decode grid for this GPU");
-  p.num_waves = std::min(waves, plan.max_pieces);
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
-  pa_status ps = launch_status("decode plan kernel");
-  if (ps != PA_OK) return ps;
-  launch_decode<T, D, G, PAGED, true>(p, dim3(unsigned((p.num_waves + 7) / 8 * 8)), st);
-  ps = launch_status("decode kernel");
-  if (ps != PA_OK) return ps;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, true>), combine_grid, dim3(kWave), 0, st, p);
+  launch_decode<T, D, G, PAGED>(p, dim3(unsigned(grid_units(p))), st);
+  pa_status ps = launch_status("decode partition kernel");
+  if (ps != PA_OK || p.num_parts <= 1) return ps;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), combine_grid, dim3(kWave), 0, st, p);
   return launch_status("decode combine kernel");
 }
 
@@ -1075,7 +789,6 @@ pa_status check_paged(const pa_decode_args* a, Plan* plan) {
   if (a->kv_dtype == PA_FP8_E4M3) {
     if (a->q_dtype != PA_F16 && a->q_dtype != PA_BF16)
       return fail(PA_E_UNSUPPORTED, "E4M3 caches need q_dtype PA_F16 or PA_BF16");
-    if (a->partition_size < 0) return fail(PA_E_UNSUPPORTED, "E4M3 caches use fixed partitions (partition_size >= 0)");
     if (!(a->k_scale > 0.f) || !(a->v_scale > 0.f) || !std::isfinite(a->k_scale) || !std::isfinite(a->v_scale))
       return fail(PA_E_INVAL, "k_scale and v_scale must be finite and positive");
     compute = a->q_dtype;
@@ -1252,11 +965,11 @@ extern "C" pa_status pa_decode(const pa_decode_args* a, pa_stream stream) {
     const dim3 cg(unsigned(int64_t(a->num_seqs) * a->num_q_heads));
     const bool d64 = a->head_dim == 64;
     if (a->q_dtype == PA_F16) {
-      if (d64) hipLaunchKernelGGL((decode_combine_kernel<F16, 64, false>), cg, dim3(kWave), 0, hs, p);
-      else hipLaunchKernelGGL((decode_combine_kernel<F16, 128, false>), cg, dim3(kWave), 0, hs, p);
+      if (d64) hipLaunchKernelGGL((decode_combine_kernel<F16, 64>), cg, dim3(kWave), 0, hs, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<F16, 128>), cg, dim3(kWave), 0, hs, p);
     } else {
-      if (d64) hipLaunchKernelGGL((decode_combine_kernel<BF16, 64, false>), cg, dim3(kWave), 0, hs, p);
-      else hipLaunchKernelGGL((decode_combine_kernel<BF16, 128, false>), cg, dim3(kWave), 0, hs, p);
+      if (d64) hipLaunchKernelGGL((decode_combine_kernel<BF16, 64>), cg, dim3(kWave), 0, hs, p);
+      else hipLaunchKernelGGL((decode_combine_kernel<BF16, 128>), cg, dim3(kWave), 0, hs, p);
     }
     return launch_status("decode combine kernel");
   }
@@ -1330,7 +1043,3 @@ extern "C" pa_status pa_decode_contiguous(const pa_contig_args* a, pa_stream str
                        a->num_kv_heads, static_cast<hipStream_t>(stream));
 }
 
-extern "C" int pa_decode_set_waves(int32_t waves) {
-  const int w = waves <= 0 ? 0 : std::max(8, std::min(kMaxWaves, waves / 8 * 8));
-  return g_waves_override.exchange(w);
-}

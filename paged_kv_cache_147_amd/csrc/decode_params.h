@@ -10,13 +10,6 @@
 
 namespace pkv {
 
-// Header of the balanced schedule, written by decode_plan_kernel.
-struct Sched {
-  int64_t total;           // tiles over all (KV head, sequence) ranges
-  int32_t tiles_per_head;  // tiles over all sequences of one KV head
-  int32_t pieces;          // pieces (= waves with work); 0 when there is no context
-};
-
 struct DecodeParams {
   void* out;
   const void* q;
@@ -24,11 +17,8 @@ struct DecodeParams {
   const char* v;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* part_o;        // fixed: [S][Hq][num_parts][D]; balanced: [2 pieces][G][D] unnormalised sums
+  float* part_o;        // [S][Hq][num_parts][D] unnormalised weighted sums of the partitions
   float* part_ml;       // same rows, (max, sum of weights) in the log2 domain
-  Sched* sched;         // balanced: schedule header
-  int32_t* cum;         // balanced: [S + 1] tiles of the sequences before s (per KV head)
-  int32_t* start_seq;   // balanced: [pieces] sequence holding each piece's first tile
   int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
   int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
   int32_t num_seqs;
@@ -39,10 +29,9 @@ struct DecodeParams {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t max_ctx;
-  int32_t part_tokens;  // fixed: partition length; balanced: chunk length
-  int32_t num_parts;    // fixed: partitions of the longest context (record slots per head)
-  int32_t full_parts;   // fixed: partitions that can be full under the bound (max_ctx / part_tokens)
-  int32_t num_waves;    // balanced: upper bound on pieces (waves launched, rounded up to 8)
+  int32_t part_tokens;  // partition length
+  int32_t num_parts;    // partitions of the longest context (record slots per head)
+  int32_t full_parts;   // partitions that can be full under the bound (max_ctx / part_tokens)
   int32_t out_f32;
   float scale_log2e;    // scale * log2(e) (times k_scale for E4M3 caches): scores live in the log2 domain
   float v_scale;        // E4M3 caches: V element = value(code) * v_scale

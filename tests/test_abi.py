@@ -164,33 +164,12 @@ def test_automatic_partition_size(S, hkv, max_ctx, expect_parts):
     assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
 
 
-@pytest.mark.parametrize("S,hkv,max_ctx", [
-    (256, 8, 4828),         # many pieces: capped at 8192
-    (4, 8, 1024),           # small batch: 4 * 8 * 64 / 8 = 256 pieces
-    (1, 1, 16),             # one tile: one piece
-])
-def test_balanced_workspace_layout(S, hkv, max_ctx):
-    # header, cum[S + 1], start_seq[pieces], then (m, l) and o records: two
-    # per piece and query head of a group (G = 4)
+@pytest.mark.parametrize("part", [-1, -8, 4, 12])
+def test_partition_size_must_be_zero_or_a_positive_multiple_of_8(part):
     lib = P.raw()
     n = ctypes.c_size_t()
-    a = _args(num_seqs=S, num_kv_heads=hkv, num_q_heads=4 * hkv, max_blocks=8192 // 16,
-              max_ctx=max_ctx, partition_size=-1)
-    assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
-    tiles = -(-max_ctx // 16)
-    pieces = max(1, min(8192, S * hkv * tiles // 8))
-    align = lambda x: (x + 255) // 256 * 256
-    recs = 2 * pieces * 4
-    assert n.value == align(16) + align((S + 1) * 4) + align(pieces * 4) + align(recs * 2 * 4) + \
-        align(recs * 128 * 4)
-
-
-def test_wave_override_round_trip():
-    lib = P.raw()
-    prev = lib.pa_decode_set_waves(100)      # rounded down to a multiple of 8
-    assert lib.pa_decode_set_waves(3) == 96  # and up to at least 8
-    assert lib.pa_decode_set_waves(0) == 8
-    assert lib.pa_decode_set_waves(prev) == 0
+    a = _args(partition_size=part)
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == L.PA_E_INVAL
 
 
 def test_prefill_rejects_before_launch():
@@ -227,7 +206,7 @@ def _fp8(**kw):
     (dict(q_dtype=L.PA_F32), L.PA_E_UNSUPPORTED),          # queries must be 16-bit
     (dict(q_dtype=9), L.PA_E_UNSUPPORTED),
     (dict(out_dtype=L.PA_F16), L.PA_E_UNSUPPORTED),        # 16-bit output must be q's type
-    (dict(partition_size=-1), L.PA_E_UNSUPPORTED),         # no balanced schedule over codes
+    (dict(partition_size=-1), L.PA_E_INVAL),               # partitions are 0 (automatic) or positive
     (dict(k_scale=0.0), L.PA_E_INVAL),
     (dict(v_scale=-1.0), L.PA_E_INVAL),
     (dict(k_scale=float("nan")), L.PA_E_INVAL),

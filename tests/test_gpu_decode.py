@@ -52,7 +52,7 @@ def test_shapes_against_oracle(dtype, d, G, B):
     print(f"[decode] {wl.name} ctx={ctx}", flush=True)
     dev = NativeDeviceRun(wl)
     ref = oracle_out(wl)
-    for part in (0, 64, 512, -1):        # -1: the balanced schedule
+    for part in (0, 64, 512):
         got = dev.decode(partition_size=part).cpu().numpy()
         assert_close(got, ref, dtype, f"{wl.name} partition {part}")
 
@@ -91,7 +91,7 @@ def test_native_dtype_output_within_one_ulp(dtype):
     ref = oracle_out(wl)
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     ref_r = torch.from_numpy(ref).to(tdt).double().numpy()      # the oracle rounded once
-    for part in (0, 128, -1):
+    for part in (0, 128, 512):
         got = dev.decode(out_dtype=tdt, partition_size=part).double().cpu().numpy()
         tol = np.maximum(np.maximum(ulp(ref_r, dtype), ulp(got, dtype)), F32_FLOOR)
         assert np.all(np.abs(got - ref_r) <= tol), part
@@ -122,9 +122,6 @@ def test_contiguous_kernel_matches_oracle_and_paged_bitwise():
         # same score path (matrix cores; at B = 8 a tile's halves come from two
         # blocks), same order of every sum: bit-identical
         assert torch.equal(out, paged), B
-        bal = torch.empty_like(out)
-        P.pa_decode_contiguous(bal, dev.q, kd, vd, torch.from_numpy(ctx).cuda(), wl.scale, partition_size=-1)
-        assert torch.equal(bal, dev.decode(partition_size=-1)), B      # balanced cuts agree too
         ref = A.contiguous_decode(wl.q, k, v, ctx, wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads)
         assert_close(out.cpu().numpy(), ref, wl.dtype, f"contiguous B={B}")
         assert_close(paged.cpu().numpy(), ref, wl.dtype, f"paged B={B}")
@@ -205,36 +202,16 @@ def test_workspace_reuse_across_calls():
     assert_close(firsts[0].cpu().numpy(), ref, "bf16", "reuse")
 
 
-# ---- balanced schedule -------------------------------------------------------
+# ---- empty contexts between long ones ------------------------------------------
 
-@pytest.fixture
-def set_waves():
-    prev = P.pa_decode_set_waves(0)
-    yield P.pa_decode_set_waves
-    P.pa_decode_set_waves(prev)
+LONG_CTX = [1, 2000, 37, 449, 896, 1500, 17, 912]
 
 
-LONG_CTX = [1, 2000, 37, 449, 896, 1500, 17, 912]   # pieces cut mid-sequence, several chunks per piece
-
-
-@pytest.mark.parametrize("dtype,d,G,B", [("bf16", 128, 4, 16), ("f16", 128, 1, 8), ("f32", 64, 8, 32),
-                                         ("bf16", 64, 2, 32), ("f16", 128, 8, 16)], ids=str)
-@pytest.mark.parametrize("nw", [8, 24, 64])
-def test_balanced_forced_waves(dtype, d, G, B, nw, set_waves):
-    # 8 waves: pieces of ~1900 tokens, each holding several whole sequences
-    # and several 448-token chunks; 64: most sequences cut into many pieces
-    set_waves(nw)
-    wl = W.independent(f"bal_{dtype}_{d}_{G}_{B}", LONG_CTX, (2 * G, 2, d, B, dtype),
-                       num_blocks=2 * 8 * 2048 // B, max_blocks=2048 // B, seed=40 + G + B)
-    print(f"[decode] {wl.name} waves={nw}", flush=True)
-    dev = NativeDeviceRun(wl)
-    assert_close(dev.decode(partition_size=-1).cpu().numpy(), oracle_out(wl), dtype, f"{wl.name} waves {nw}")
-
-
-def test_balanced_mixed_empty_contexts(set_waves):
-    # empty and negative contexts between real ones: zero rows, and the
-    # pieces skip them
-    wl = W.independent("bal_empty", LONG_CTX, (8, 2, 128, 16, "bf16"), 2048, 128, seed=3)
+@pytest.mark.parametrize("part", [0, 64, 512])
+def test_mixed_empty_and_long_contexts(part):
+    # empty and negative contexts between real ones: zero rows; the others
+    # span one to 32 partitions
+    wl = W.independent("mixed_empty", LONG_CTX, (8, 2, 128, 16, "bf16"), 2048, 128, seed=3)
     dev = NativeDeviceRun(wl)
     lens = np.array([1, 0, 37, -3, 896, 0, 17, 911], dtype=np.int32)   # within each sequence's tokens
     run = OracleRun(wl)
@@ -242,51 +219,29 @@ def test_balanced_mixed_empty_contexts(set_waves):
     live = [(s, h) for s in range(wl.num_seqs) if lens[s] > 0 for h in range(wl.num_q_heads)]
     ref = A.paged_decode(wl.q, run.cache.k, run.cache.v, tables, np.maximum(lens, 0), wl.block_size,
                          wl.scale, wl.dtype, wl.num_q_heads, wl.num_kv_heads, heads=live)
-    for nw in (0, 8, 16):
-        set_waves(nw)
-        got = dev.decode(ctx=torch.from_numpy(lens).cuda(), partition_size=-1).cpu().numpy()
-        assert np.all(got[lens <= 0] == 0)
-        assert_close(got, ref, "bf16", f"empty contexts, waves {nw}")
-
-
-def test_balanced_workspace_reuse_and_determinism(set_waves):
-    wl = W.independent("bal_reuse", LONG_CTX, (16, 4, 128, 16, "bf16"), 2048, 128, seed=5)
-    dev = NativeDeviceRun(wl)
-    ref = oracle_out(wl)
-    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), device="cuda")
-    for nw in (0, 8):
-        set_waves(nw)
-        ws = None
-        firsts = []
-        for rep in range(3):
-            ws = P.pa_decode(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, wl.scale,
-                             partition_size=-1, workspace=ws)
-            firsts.append(out.clone())
-            short = torch.clamp(dev.ctx - 300, min=1)      # a different cut in between
-            P.pa_decode(out, dev.q, dev.k_cache, dev.v_cache, dev.tables, short, wl.scale,
-                        partition_size=-1, workspace=ws)
-        assert all(torch.equal(firsts[0], f) for f in firsts[1:])
-        assert_close(firsts[0].cpu().numpy(), ref, "bf16", f"reuse, waves {nw}")
+    got = dev.decode(ctx=torch.from_numpy(lens).cuda(), partition_size=part).cpu().numpy()
+    assert np.all(got[lens <= 0] == 0)
+    assert_close(got, ref, "bf16", f"empty contexts, partition {part}")
 
 
 @pytest.mark.parametrize("share", [True, False], ids=["shared_prefix", "no_share"])
 def test_full_size_gqa_sampled(share):
     # the benchmarked workload (Llama-3.1-8B layer, 256 sequences) in the
-    # benchmarked launch (automatic fixed partitions) and with the balanced
-    # schedule; 50 (sequence, head) rows checked against the oracle one by one
+    # benchmarked launch (automatic fixed partitions) and in 128-token
+    # partitions; 50 (sequence, head) rows checked against the oracle one by one
     wl = W.llama31_8b_gqa(share=share)
     print(f"[decode] {wl.name} full size", flush=True)
     dev = NativeDeviceRun(wl)
     got = dev.decode().cpu().numpy()
-    bal = dev.decode(partition_size=-1).cpu().numpy()
+    p128 = dev.decode(partition_size=128).cpu().numpy()
     rng = np.random.default_rng(11)
     pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, wl.num_seqs, 48), rng.integers(0, wl.num_q_heads, 48))]
     pairs += [(0, 0), (wl.num_seqs - 1, wl.num_q_heads - 1)]
     ref = oracle_out(wl, heads=pairs)
     idx = tuple(np.array(pairs).T)
     assert_close(got[idx], ref[idx], wl.dtype, wl.name)
-    assert_close(bal[idx], ref[idx], wl.dtype, wl.name + " balanced")
-    assert np.isfinite(got).all() and np.isfinite(bal).all()
+    assert_close(p128[idx], ref[idx], wl.dtype, wl.name + " 128-token partitions")
+    assert np.isfinite(got).all() and np.isfinite(p128).all()
 
 
 # ---- debug validation --------------------------------------------------------

@@ -254,7 +254,7 @@ def test_decode_refuses_unsupported_arguments():
     wl = W.independent("fp8_bad", [5], (4, 2, 128, 16, "bf16"), num_blocks=4, max_blocks=4, seed=1)
     case = Fp8Case(wl)
     with pytest.raises(P.PagedKVError):
-        case.decode(partition_size=-1)                    # balanced schedule: not for E4M3
+        case.decode(partition_size=-1)                    # partitions are 0 (automatic) or positive
     for ks in (0.0, float("nan")):
         with pytest.raises(P.PagedKVError):
             out = torch.empty((1, 4, 128), dtype=torch.float32, device="cuda")
