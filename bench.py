@@ -654,6 +654,8 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode
         f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
     gbps = kv / (ms_step * 1e-3) / 1e9
     achieved = alg / (dec_avg * 1e-3) / 1e9
+    traffic = measured_fp8_traffic(workload + "_fp8")
+    hbm_gbps = traffic / (dec_avg * 1e-3) / 1e9 if traffic else None
     res = {
         "metric": FP8_METRIC,
         "value": round(gbps, 2),
@@ -674,7 +676,9 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode
         "decode_speedup_vs_bf16": round(bf16_decode_ms / dec_avg, 3) if bf16_decode_ms else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_fp8_traffic(workload + "_fp8"),
+                     "traffic": traffic,
+                     "hbm_gbps": round(hbm_gbps, 2) if hbm_gbps else None,
+                     "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4) if hbm_gbps else None,
                      "kernel": "pa_decode over E4M3 codes (partition + combine launches)",
                      "avg_launch_ms": round(dec_avg, 5), "bytes_per_launch": alg,
                      "launch_ms_p10_median_p90": [round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)]},
