@@ -39,11 +39,13 @@
 //     the LDS tile through ds_read_b64_tr_b16, the gfx950 transposing load
 //     (each 16-lane group reads 4 rows x 16 columns and every lane receives
 //     one column of 4);
-//   * for a bf16 cache P is split into a bf16 high part and the bf16
-//     rounding of the remainder, two MFMAs per block, so p.V keeps ~16 bits
-//     of P (one bf16 rounding, 8 bits, leaves a relative L2 error near
-//     1e-3); an f16 P, rounded once, keeps 11 bits, which is enough, so an
-//     f16 cache takes one MFMA per block;
+//   * P enters p.V rounded once to f16 (11 significant bits; one bf16
+//     rounding, 8 bits, would leave a relative L2 error near 1e-3), one MFMA
+//     per block.  A bf16 cache's V rows are turned into f16 in LDS once per
+//     step by the whole workgroup (exact inside the f16 range).  A V value
+//     beyond that range becomes inf and leaves a non-finite O; a workgroup
+//     that ends so runs again on bf16 V rows with P split into a bf16 high
+//     part and the bf16 rounding of the rest (~16 bits), two MFMAs per block;
 //   * workgroups are issued longest first (the last chunk blocks see the
 //     most keys), so the short ones fill the tail.
 #include "device_common.h"
@@ -198,10 +200,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   static_assert(TILE % (kThreads * 16) == 0, "a step's tile must split into whole wave loads");
   static_assert(kStages == 4, "steps go in pairs: two stages computed while two fill");
 
-  // bf16 probabilities go in as two 16-bit parts, f16 ones as one
-  constexpr bool kSplit = std::is_same<T, BF16>::value;
+  // bf16 caches: each step's V rows are turned into f16 in LDS once per
+  // workgroup, so that p.V takes P rounded once to f16 (one MFMA per block).
+  // A workgroup whose V holds a value beyond the f16 range runs again on
+  // bf16 V rows with P split into two bf16 parts.
+  constexpr bool kConvV = std::is_same<T, BF16>::value;
 
   __shared__ __align__(16) char lds[kStages][2][TILE];   // [stage][K, V][32 rows]
+  __shared__ int vflag;                                  // some O not finite after the f16 pass
 
   const int tid = threadIdx.x;
 
@@ -391,16 +397,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const float slack = kSlack / c;         // kSlack in raw score units
   float run_m[kSub], run_mc[kSub], run_l[kSub];   // running max (raw), times c, this lane's part of the sum
   f32x4_t o[kSub][NN];                    // O^T: lane holds columns 16 nn + 4 q4 + i of row m16
+  auto clear_state = [&]() {
 #pragma unroll
-  for (int j = 0; j < kSub; ++j) {
-    run_m[j] = run_mc[j] = -INFINITY;
-    run_l[j] = 0.f;
+    for (int j = 0; j < kSub; ++j) {
+      run_m[j] = run_mc[j] = -INFINITY;
+      run_l[j] = 0.f;
 #pragma unroll
-    for (int nn = 0; nn < NN; ++nn) o[j][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int nn = 0; nn < NN; ++nn) o[j][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  clear_state();
 
-  auto compute = [&](int step, auto masked_step) {
+  auto compute = [&](int step, auto masked_step, auto split_step) {
     constexpr bool masked = decltype(masked_step)::value;   // some row of the wave stops inside this step
+    constexpr bool psplit = decltype(split_step)::value;    // bf16 V rows: P as two bf16 parts
     const int t0 = step * kKeys;
     const char* kt = lds[step % kStages][0];
     const char* vt = lds[step % kStages][1];
@@ -451,13 +461,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       // 16 + 4 q4 + e - 4 (e >= 4), i.e. exactly pr[e].
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if constexpr (kSplit) {
+        if constexpr (psplit) {
           uint32_t hi, lo;
-          split(T{}, pr[2 * e], pr[2 * e + 1], hi, lo);
+          split(BF16{}, pr[2 * e], pr[2 * e + 1], hi, lo);
           PH[j][e] = hi;
           PL[j][e] = lo;
         } else {
-          PH[j][e] = pack2(T{}, pr[2 * e], pr[2 * e + 1]);
+          PH[j][e] = pack2(F16{}, pr[2 * e], pr[2 * e + 1]);
         }
       }
     }
@@ -471,8 +481,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const u32x4_t va = {w0.x, w0.y, w1.x, w1.y};
 #pragma unroll
       for (int j = 0; j < kSub; ++j) {
-        o[j][nn] = mfma(T{}, va, PH[j], o[j][nn]);
-        if constexpr (kSplit) o[j][nn] = mfma(T{}, va, PL[j], o[j][nn]);
+        if constexpr (psplit) {
+          o[j][nn] = mfma(BF16{}, va, PH[j], o[j][nn]);
+          o[j][nn] = mfma(BF16{}, va, PL[j], o[j][nn]);
+        } else {
+          o[j][nn] = mfma(F16{}, va, PH[j], o[j][nn]);
+        }
       }
     }
   };
@@ -483,20 +497,86 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // steps st + 2 and st + 3, held the previous pair, which every wave has
   // finished.  The next pair's loads are in flight while this pair is
   // computed, and there is one barrier per two steps.
-  for (int st = 0; st < nsteps; st += 2) {
-    wait_and_meet<0>();
-    if (st + 2 < nsteps) issue(st + 2);
-    if (st + 3 < nsteps) issue(st + 3);
-    if (st + 4 < nsteps) fetch(st + 4);
-    if (st + 5 < nsteps) fetch(st + 5);
+  // bf16 -> f16 of the pair's V rows in place (each thread its own 16-byte
+  // pieces; a piece holds 8 elements of one row wherever the swizzle put
+  // it), exact for every bf16 value inside the f16 range; a value beyond it
+  // becomes inf.  The barrier waits for the LDS traffic only, so the next
+  // pair's ring loads stay in flight.
+  auto convert_v = [&](int st) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int s2 = st + h;
-      if (s2 < nsteps && s2 * kKeys <= wave_last) {
-        if (s2 * kKeys + kKeys - 1 > wave_first) compute(s2, std::true_type{});
-        else compute(s2, std::false_type{});
+      if (st + h >= nsteps) break;
+      char* vt = lds[(st + h) % kStages][1];
+#pragma unroll
+      for (int cch = 0; cch < TILE / (kThreads * 16); ++cch) {
+        u32x4_t* w = reinterpret_cast<u32x4_t*>(vt + (cch * kThreads + tid) * 16);
+        const u32x4_t x = *w;
+        u32x4_t y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = pack2(F16{}, __uint_as_float(x[e] << 16), __uint_as_float(x[e] & 0xffff0000u));
+        *w = y;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // All steps of the workgroup, pair by pair; for a bf16 cache in the first
+  // mode the V rows of each pair are turned into f16 first.
+  auto ring_loop = [&](auto split_mode) {
+    constexpr bool psplit = decltype(split_mode)::value;
+    for (int st = 0; st < nsteps; st += 2) {
+      wait_and_meet<0>();
+      if (st + 2 < nsteps) issue(st + 2);
+      if (st + 3 < nsteps) issue(st + 3);
+      // before the block-id loads below: the conversion's wait for LDS
+      // traffic would also wait for them (scalar loads share the counter)
+      if constexpr (kConvV && !psplit) convert_v(st);
+      if (st + 4 < nsteps) fetch(st + 4);
+      if (st + 5 < nsteps) fetch(st + 5);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int s2 = st + h;
+        if (s2 < nsteps && s2 * kKeys <= wave_last) {
+          if (s2 * kKeys + kKeys - 1 > wave_first) compute(s2, std::true_type{}, split_mode);
+          else compute(s2, std::false_type{}, split_mode);
+        }
+      }
+    }
+  };
+
+  if constexpr (kConvV) {
+    if (tid == 0) vflag = 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ring_loop(std::false_type{});
+    // A V value beyond the f16 range became inf, and every V row of a staged
+    // step is multiplied by some probability (0 for masked keys, and
+    // 0 * inf is NaN), so it leaves a non-finite value in O.  If any wave's
+    // O is not finite, the workgroup runs its steps again with bf16 V rows
+    // and P split in two bf16 parts (inputs that hold NaN or inf themselves
+    // take that path too, and give its result).  The loop ended on a drained
+    // ring.
+    float osum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSub; ++j)
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) osum += (o[j][nn][0] + o[j][nn][1]) + (o[j][nn][2] + o[j][nn][3]);
+    if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(osum))) vflag = 1;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (__builtin_amdgcn_readfirstlane(vflag)) {
+      clear_state();
+      fetch(0);
+      issue(0);
+      if (1 < nsteps) {
+        fetch(1);
+        issue(1);
+      }
+      if (2 < nsteps) fetch(2);
+      if (3 < nsteps) fetch(3);
+      ring_loop(std::true_type{});
+    }
+  } else {
+    ring_loop(std::false_type{});
   }
 
   // the loop's last wait drained the ring; rows of the wave now end

@@ -84,13 +84,12 @@ def test_prefill_native_dtype_output_within_one_step_of_the_probability_bound(dt
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     got = run.run(out_dtype=tdt).double().cpu().numpy()
     ref = torch.from_numpy(oracle_rows(wl)).to(tdt).double().numpy()
-    # The p.V product takes P rounded to the cache's 16-bit type: for bf16 as
-    # a high part plus the rounding of the rest, |dP| <= 2^-(2m+2) P with
-    # m = 7 mantissa bits; for f16 as one rounded value, |dP| <= 2^-(m+1) P
-    # with m = 10.  The output, a P-weighted mean of V rows, then moves by
-    # at most that factor times max|V|, on top of its own final rounding.
+    # The p.V product takes P rounded once to f16 (a bf16 cache's V rows are
+    # turned into f16 first, exactly, as every value here is inside the f16
+    # range): |dP| <= 2^-11 P.  The output, a P-weighted mean of V rows, then
+    # moves by at most 2^-11 max|V|, on top of its own final rounding.
     from oracle.bits import to_f64
-    rel = 2.0 ** -16 if dtype == "bf16" else 2.0 ** -11
+    rel = 2.0 ** -11
     bound = rel * np.abs(to_f64(wl.v_rows, dtype)).max()
     tol = np.maximum(ulp(ref, dtype), ulp(got, dtype)) + max(F32_FLOOR, bound)
     bad = np.abs(got - ref) > tol
@@ -102,6 +101,37 @@ def test_prefill_native_dtype_output_within_one_step_of_the_probability_bound(dt
             print("row", t, "got", got[t], "ref_rounded", ref[t], "oracle", ref64[t], "ulp", tol[t], flush=True)
         print("count", int(bad.sum()), "of", bad.size, flush=True)
     assert not bad.any()
+
+
+def test_prefill_bf16_values_beyond_the_f16_range():
+    # A bf16 cache's V rows go into p.V as f16; a pair of steps whose rows
+    # hold a value beyond the f16 range sends its workgroup back to the start
+    # on bf16 rows with P in two bf16 parts.  Here KV head 0 of sequence 3
+    # gets rows around token 200 scaled by 2^17 (so the restart happens after
+    # several f16 pairs); its chunk rows that see them take the bf16 path,
+    # every other workgroup stays on f16.  Both are checked against the
+    # oracle, the scaled rows relative to their largest |V|.
+    wl = W.prefill_chunks("pf_wide", PREFIX, CHUNK, (8, 2, 128, 16, "bf16"), 2 * 6 * 512 // 16, 512 // 16, seed=11)
+    r0 = next(op[3] for op in wl.setup_ops if op[0] == "alloc" and op[1] == 3)    # sequence 3's prefix rows
+    rows = np.arange(r0 + 196, r0 + 214)
+    v = wl.v_rows[rows, 0]                                # KV head 0, bf16 bits
+    exp = (v >> 7) & 0xFF
+    ok = (exp > 0) & (exp < 200)
+    v[ok] = v[ok] + np.uint16(17 << 7)                    # times 2^17, exactly
+    wl.v_rows[rows, 0] = v
+    from oracle.bits import to_f64
+    assert np.abs(to_f64(wl.v_rows, "bf16")).max() > 65504
+    run = PrefillRun(wl)
+    got = run.run().cpu().numpy()
+    ref = oracle_rows(wl)
+    G = wl.num_q_heads // wl.num_kv_heads
+    qs = wl.info["q_start"]
+    wide = np.zeros(got.shape[:2], dtype=bool)
+    wide[qs[3]:qs[4], :G] = True                          # sequence 3's rows, query heads of KV head 0
+    big = np.abs(to_f64(wl.v_rows[:, 0], "bf16")).max()
+    assert_close(got[wide] / big, ref[wide] / big, "bf16", "rows over V beyond the f16 range")
+    assert_close(got[~wide], ref[~wide], "bf16", "every other row")
+    assert np.abs(ref[wide]).max() > 1000                 # the scaled rows did reach the outputs
 
 
 def test_prefill_one_row_chunks_match_decode():
