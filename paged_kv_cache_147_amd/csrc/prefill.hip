@@ -32,7 +32,9 @@
 //     max moves only when a score exceeds it by more than 2^8 (until then the
 //     probabilities are exponentials against the stale max, at most 2^8, and
 //     the final division by the sum, taken against the same max, cancels
-//     it), the sum is kept per lane and added across lanes once at the end;
+//     it); the row sums of the probabilities come from the matrix cores,
+//     one more block of the p.V product with V^T replaced by ones, so they
+//     sum exactly the rounded probabilities that went into O;
 //   * the same 8 probabilities per lane are, unchanged, the B operand of
 //     O^T += V^T P^T -- with the contraction's 32 keys ordered so that lane
 //     group q holds keys 4q..4q+3 and 16+4q..16+4q+3 -- and V^T comes from
@@ -94,8 +96,8 @@ __device__ __forceinline__ void split(BF16, float a, float b, uint32_t& hi, uint
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){ra, rb}, bf16x2_t));
 }
 
-// Max / sum with the lane 16 or 32 positions away: after a permlane swap of
-// x with itself the two results hold x of the lane and of its partner.
+// Max with the lane 16 or 32 positions away: after a permlane swap of x with
+// itself the two results hold x of the lane and of its partner.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
@@ -103,14 +105,6 @@ __device__ __forceinline__ float max_xor16(float x) {
 __device__ __forceinline__ float max_xor32(float x) {
   const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // Chunk permutation of a staged row: a row of CPR 16-byte chunks keeps chunk
@@ -395,13 +389,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 
   const float c = fmaxf(fabsf(p.scale_log2e), 1e-30f);
   const float slack = kSlack / c;         // kSlack in raw score units
-  float run_m[kSub], run_mc[kSub], run_l[kSub];   // running max (raw), times c, this lane's part of the sum
+  float run_m[kSub], run_mc[kSub];        // running max (raw), and times c
+  // Running sums of the probabilities, from the matrix cores: one more block
+  // of the p.V product with an all-ones V^T, so every element of run_l[j]
+  // is row m16's sum of the very (rounded) P that went into O.
+  f32x4_t run_l[kSub];
   f32x4_t o[kSub][NN];                    // O^T: lane holds columns 16 nn + 4 q4 + i of row m16
   auto clear_state = [&]() {
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
       run_m[j] = run_mc[j] = -INFINITY;
-      run_l[j] = 0.f;
+      run_l[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) o[j][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -455,7 +453,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -run_mc[j]));
-        run_l[j] += pr[e];
       }
       // P^T operand: contraction index 8 q4 + e is key 4 q4 + e (e < 4) or
       // 16 + 4 q4 + e - 4 (e >= 4), i.e. exactly pr[e].
@@ -487,6 +484,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         } else {
           o[j][nn] = mfma(F16{}, va, PH[j], o[j][nn]);
         }
+      }
+    }
+    // the row sums: V^T replaced by ones (1.0 in the operand's type)
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      if constexpr (psplit) {
+        const u32x4_t one = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+        run_l[j] = mfma(BF16{}, one, PH[j], run_l[j]);
+        run_l[j] = mfma(BF16{}, one, PL[j], run_l[j]);
+      } else {
+        const u32x4_t one = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+        run_l[j] = mfma(F16{}, one, PH[j], run_l[j]);
       }
     }
   };
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // the loop's last wait drained the ring; rows of the wave now end
 #pragma unroll
   for (int j = 0; j < kSub; ++j) {
-    const float l = sum_xor32(sum_xor16(run_l[j]));     // the row's 4 lanes' parts
+    const float l = run_l[j][0];
     if (!row_ok[j]) continue;
     const float inv = 1.f / l;
     const int64_t orow = (int64_t(r0 + tok[j]) * p.num_q_heads + head) * D;
