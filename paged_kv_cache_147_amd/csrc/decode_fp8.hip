@@ -9,9 +9,10 @@
 // decode_fp8_kernel: one wave per (partition, KV head, sequence) unit of the
 // fixed-partition schedule, writing the same outputs and records as
 // decode_kernel, with both contractions on the matrix cores.  Every E4M3
-// value is exactly a float16 and a bfloat16 value, so codes are widened to
-// q's 16-bit type without rounding; the only roundings are the float32
-// accumulation's and the probabilities' 16-bit split.
+// value is exactly a float16 and a bfloat16 value, so codes are widened
+// without rounding: K to q's 16-bit type, V to f16 whatever q's type, so
+// that p.V takes P rounded once to f16 (11 significant bits); the only other
+// roundings are the float32 accumulation's.
 //
 // Per 32-token step, lane (m16 = lane % 16, q4 = lane / 16), written for
 // head_dim 128 (at 64: two score steps, one 16-byte K piece, 4 V bytes per
@@ -31,8 +32,8 @@
 //     in place.  V^T needs those 8 tokens of one column in a lane: lane
 //     (m16, q4) loads 8 bytes (columns 8 m16 .. 8 m16 + 7) of each of its 8
 //     rows and regroups bytes into token pairs in registers, so output block
-//     nn of O^T is head_dim column 8 m16 + nn.  P enters as a 16-bit high
-//     part plus the 16-bit rounding of its remainder (two MFMAs).
+//     nn of O^T is head_dim column 8 m16 + nn.  V codes widen to f16 and P
+//     enters rounded once to f16: one f16 MFMA per block.
 // Rows are read with buffer loads from a scalar resource per 16-token span and
 // a fixed per-lane offset (global loads with per-lane addresses when 8-token
 // blocks put two blocks in a span); two steps of loads are in flight
@@ -99,20 +100,6 @@ __device__ __forceinline__ uint32_t pair_even(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t pair_odd(uint32_t a, uint32_t b) {
   return ((a >> 8) & 0x00ff00ffu) | (b & 0xff00ff00u);
-}
-
-// Two probabilities -> a packed 16-bit high part (round to nearest even) and
-// the packed 16-bit rounding of what the high part leaves out.
-__device__ __forceinline__ void split_p(BF16, float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf162_t));
-  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){ra, rb}, bf162_t));
-}
-__device__ __forceinline__ void split_p(F16, float a, float b, uint32_t& hi, uint32_t& lo) {
-  const f16x2_t h = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const f32x2_t hw = __builtin_convertvector(h, f32x2_t);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - hw.x, b - hw.y}, f16x2_t));
 }
 
 // Max / sum with the lane 16 or 32 positions away (the same head's lanes).
@@ -306,16 +293,14 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) o[nn] *= f;
     }
-    u32x4_t ph, pl;
+    // P rounded once to f16 (11 significant bits), whatever q's type
+    u32x4_t ph;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * e], c, -run_mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * e + 1], c, -run_mc));
       run_l += p0 + p1;
-      uint32_t hi, lo;
-      split_p(T{}, p0, p1, hi, lo);
-      ph[e] = hi;
-      pl[e] = lo;
+      ph[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p0, p1}, f16x2_t));
     }
     // V rows e = 0..7 of the lane: tokens 4 q4 + e (e < 4), 16 + 4 q4 + e - 4
     uint2 vr[8];
@@ -332,16 +317,13 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
         const uint32_t a = half ? vr[2 * i].y : vr[2 * i].x;
         const uint32_t bb = half ? vr[2 * i + 1].y : vr[2 * i + 1].x;
         const uint32_t ev = pair_even(a, bb), od = pair_odd(a, bb);
-        va[0][i] = e4m3_pair<false>(T{}, ev);
-        va[1][i] = e4m3_pair<false>(T{}, od);
-        va[2][i] = e4m3_pair<true>(T{}, ev);
-        va[3][i] = e4m3_pair<true>(T{}, od);
+        va[0][i] = e4m3_pair<false>(F16{}, ev);
+        va[1][i] = e4m3_pair<false>(F16{}, od);
+        va[2][i] = e4m3_pair<true>(F16{}, ev);
+        va[3][i] = e4m3_pair<true>(F16{}, od);
       }
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        o[4 * half + n] = mfma(T{}, va[n], ph, o[4 * half + n]);
-        o[4 * half + n] = mfma(T{}, va[n], pl, o[4 * half + n]);
-      }
+      for (int n = 0; n < 4; ++n) o[4 * half + n] = mfma(F16{}, va[n], ph, o[4 * half + n]);
     }
   };
   auto step = [&](const Fp8Rows<D>& b, int st) {
