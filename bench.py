@@ -26,7 +26,9 @@ Nested objects in the same line:
   prefill      pa_prefill on the Llama-3.1-8B-like prefill batch, TFLOP/s
                against the dense bf16 matrix-core peak;
   prefix_cache, swap, fp8   the prefix cache, the preemption copies, and the
-               decode step over an E4M3 copy of the cache.
+               decode step over an E4M3 copy of the cache;
+  configs      the Llama-7B-like MHA step, the LLaMA-13B-like layer at
+               context 4096 and its 4-beam copy-on-write batch.
 ``--mode decode|prefill|prefix|swap|fp8|ceiling`` prints one alone.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -883,6 +885,31 @@ def time_contiguous(wl, run, steps, nrep, dev, partition_size=0):
             "overhead_identity_vs_contiguous": round(ident_ms / contig_ms - 1, 4)}
 
 
+def bench_configs(dev, steps, warmup, nrep):
+    """The other decode configurations of the scope, each a full step (copies,
+    pa_write_kv, pa_decode) at its real size: the Llama-7B-like MHA layer, the
+    LLaMA-13B-like layer at context 4096, and its 4-beam batch with the step's
+    copy-on-write copies.  Same timing as the headline line."""
+    import torch
+
+    import workloads as W
+    out = {}
+    for name in ("llama7b_mha", "llama13b_long", "llama13b_beam"):
+        key, desc = WORKLOADS[name]
+        wl = W.CONFIGS[key]()
+        res, run, _ = bench_decode_step(wl, name, desc, dev, steps, warmup, nrep)
+        del run
+        torch.cuda.empty_cache()
+        r = res["roofline"]
+        out[name] = {"description": desc, "batch": wl.num_seqs, "heads": [wl.num_q_heads, wl.num_kv_heads],
+                     "kv_dtype": wl.dtype, "ctx_mean": res["config"]["ctx_mean"],
+                     "kv_bytes_per_step": res["config"]["kv_bytes_per_step"],
+                     "ms_per_step": res["ms_per_step"], "step_gbps": res["value"], "seqs_per_s": res["seqs_per_s"],
+                     "decode_ms": r["avg_launch_ms"], "decode_seqs_per_s": res["decode_seqs_per_s"],
+                     "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac")}}
+    return out
+
+
 def bench_block_sweep(dev, steps, nrep):
     """Block sizes 8 / 16 / 32 on 128 sequences at ctx 1000 (GQA 32 / 8, d 128,
     bf16, identical logical Q/K/V for every B): the paged call, the
@@ -1080,6 +1107,7 @@ def main():
                                   cpu.get("fp8"), bf16_decode_ms=dec_avg)
         del run
         torch.cuda.empty_cache()
+        result["configs"] = bench_configs(dev, min(max(args.steps, 20), 100), args.warmup, args.replicas)
         result["block_sweep"] = bench_block_sweep(dev, max(args.steps, 50), args.replicas)
         result["ceiling"] = bench_ceiling(dev)
         result["prefill"] = bench_prefill(wl_pf, args.prefill_steps, args.prefill_warmup, dev, cpu.get("prefill"))
