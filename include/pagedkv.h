@@ -424,7 +424,12 @@ pa_status pa_decode_static(const pa_decode_args* args, pa_stream stream);
  * prefill works on large query blocks; "Paged Attention" (daiw.org), 回顾与衔接:
  * a tiled kernel must read K/V through the block table).  Scores and p.V run
  * on the matrix cores with float32 accumulation; the probabilities enter p.V
- * as a 16-bit value plus the 16-bit rounding of its remainder.
+ * rounded once to f16, against V rows in f16 (a bf16 cache's rows are
+ * converted exactly in on-chip memory).  A workgroup whose bf16 V rows hold a
+ * value beyond the f16 range recomputes its rows with bf16 V and each
+ * probability as a bf16 value plus the bf16 rounding of its remainder.
+ * PA_E_UNSUPPORTED also when one cache block (Hkv * B * head_dim * 2 bytes)
+ * reaches 4 GiB.
  */
 typedef struct pa_prefill_args {
   void* out;                   /* [T][Hq][head_dim], out_dtype */

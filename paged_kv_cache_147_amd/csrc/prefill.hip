@@ -128,28 +128,29 @@ __device__ __forceinline__ void wait_and_meet() {
 }
 
 // One ring load: 16 bytes from base + off (base the same for the whole wave,
-// off per lane) into LDS at lds + 16 * lane (lds the same for the whole
-// wave), by global_load_lds_dwordx4 with a scalar base, whose LDS address is
-// M0 (saved and restored here).  It is issued from asm so that the compiler, which cannot tell
-// which stage a load targets, adds no waits of its own for it in front of
-// the LDS reads: the ring's waits are wait_and_meet above.
-__device__ __forceinline__ void ring_load(const char* base, uint32_t off, const char* lds) {
+// off per lane) into LDS at lds + 16 * lane (lds, an LDS byte address, the
+// same for the whole wave), by global_load_lds_dwordx4 with a scalar base,
+// whose LDS address is M0 (saved and restored here).  It is issued from asm
+// so that the compiler, which cannot tell which stage a load targets, adds no
+// waits of its own for it in front of the LDS reads: the ring's waits are
+// explicit.  Hazards: the base is copied by a scalar move inside the asm, so
+// the load never reads a scalar register that a vector instruction (a
+// readfirstlane) wrote just before, and that move is also the one wait state
+// a load-to-LDS needs after the scalar write of M0.
+__device__ __forceinline__ void ring_load(const char* base, uint32_t off, uint32_t lds) {
   // Both are the same in every lane; readfirstlane puts them in scalar
   // registers.  It returns a signed int: each half is taken back through
   // uint32_t, so the low half of the address is zero-extended, never
   // sign-extended into the high half.
-  const uint32_t l = uint32_t(
-      __builtin_amdgcn_readfirstlane(int(uint32_t(size_t((__attribute__((address_space(3))) const char*)lds)))));
+  const uint32_t l = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
   const uint64_t b = uint64_t(uintptr_t(base));
   const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b))));
   const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32))));
   const uint64_t sb = (uint64_t(hi) << 32) | uint64_t(lo);
   uint32_t saved;
-  // s_nop 4 gives the 5 wait states a vector-ALU write of the base's scalar
-  // registers (readfirstlane) needs before a memory instruction reads them;
-  // the compiler's hazard checks do not look inside this asm.
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(off), "s"(sb), "s"(l) : "memory");
+  uint64_t copy;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_mov_b64 %1, %3\n\tglobal_load_lds_dwordx4 %2, %1\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved), "=&s"(copy) : "v"(off), "s"(sb), "s"(l) : "memory");
 }
 
 // float32 pair -> packed 16-bit pair, round to nearest even.
@@ -310,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int last_blk = (ctx - 1) >> p.log2_block;
   const int last_row = (ctx - 1) & bmask;
   const int64_t head_off = int64_t(g) * p.tile_bytes;
-  const int64_t blk_stride = int64_t(p.num_kv_heads) * p.tile_bytes;
+  const uint32_t blk_stride = uint32_t(p.num_kv_heads) * uint32_t(p.tile_bytes);   // < 2^32 (checked on the host)
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) const char*)&lds[0][0][0]));
   // The block ids of a step are fetched (scalar loads) a pair of steps
   // before its loads are issued, so their latency hides behind the math.
   // ids[step % 2] holds them.
@@ -331,10 +333,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const int blk = min(max(ids[step & 1][c], 0), p.num_blocks - 1);
       const int cap = bidx == last_blk ? last_row : bmask;
       const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
-      const int64_t at = int64_t(blk) * blk_stride + head_off;
-      const int dst = (c * kWaves + wv) * kWave * 16;
-      ring_load(p.k + at, off, lds[step % kStages][0] + dst);
-      ring_load(p.v + at, off, lds[step % kStages][1] + dst);
+      const int64_t at = int64_t(uint64_t(uint32_t(blk)) * blk_stride) + head_off;
+      const uint32_t dst = lds0 + uint32_t(step % kStages) * (2 * TILE) + uint32_t((c * kWaves + wv) * kWave * 16);
+      ring_load(p.k + at, off, dst);
+      ring_load(p.v + at, off, dst + TILE);
     }
   };
 
@@ -506,11 +508,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // steps st + 2 and st + 3, held the previous pair, which every wave has
   // finished.  The next pair's loads are in flight while this pair is
   // computed, and there is one barrier per two steps.
-  // bf16 -> f16 of the pair's V rows in place (each thread its own 16-byte
-  // pieces; a piece holds 8 elements of one row wherever the swizzle put
-  // it), exact for every bf16 value inside the f16 range; a value beyond it
-  // becomes inf.  The barrier waits for the LDS traffic only, so the next
-  // pair's ring loads stay in flight.
+  // bf16 -> f16 of the pair's V rows in place, exact for every bf16 value
+  // inside the f16 range; a value beyond it becomes inf.  Each thread turns
+  // the very 16-byte pieces that its own ring loads wrote (a piece holds 8
+  // elements of one row wherever the swizzle put it), so it needs only its
+  // own wait for them, before the pair's barrier, and the barrier then
+  // publishes the converted rows too.
   auto convert_v = [&](int st) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -527,7 +530,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         *w = y;
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   // All steps of the workgroup, pair by pair; for a bf16 cache in the first
@@ -535,12 +537,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   auto ring_loop = [&](auto split_mode) {
     constexpr bool psplit = decltype(split_mode)::value;
     for (int st = 0; st < nsteps; st += 2) {
-      wait_and_meet<0>();
+      if constexpr (kConvV && !psplit) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's pieces of the pair
+        convert_v(st);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        wait_and_meet<0>();
+      }
       if (st + 2 < nsteps) issue(st + 2);
       if (st + 3 < nsteps) issue(st + 3);
-      // before the block-id loads below: the conversion's wait for LDS
-      // traffic would also wait for them (scalar loads share the counter)
-      if constexpr (kConvV && !psplit) convert_v(st);
       if (st + 4 < nsteps) fetch(st + 4);
       if (st + 5 < nsteps) fetch(st + 5);
 #pragma unroll
@@ -637,6 +642,8 @@ pa_status check_prefill(const pa_prefill_args* a) {
     return fail(PA_E_UNSUPPORTED, "block_size must be 8, 16 or 32");
   if (a->max_blocks <= 0 || a->num_blocks <= 0) return fail(PA_E_INVAL, "max_blocks and num_blocks must be positive");
   if (a->max_chunk < 0) return fail(PA_E_INVAL, "max_chunk must be >= 0");
+  if (int64_t(a->num_kv_heads) * a->block_size * a->head_dim * 2 > int64_t(UINT32_MAX))
+    return fail(PA_E_UNSUPPORTED, "a cache block must stay under 4 GiB");
   if (!std::isfinite(a->scale)) return fail(PA_E_INVAL, "scale must be finite");
   const int64_t rbs = (int64_t(a->max_chunk) + tokens_per_workgroup(G) - 1) / tokens_per_workgroup(G);
   const int64_t units = int64_t(a->num_seqs) * a->num_kv_heads;

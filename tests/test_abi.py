@@ -190,6 +190,11 @@ def test_prefill_rejects_before_launch():
         setattr(a, field, bad)
         assert lib.pa_prefill(ctypes.byref(a), None) == code, field
         setattr(a, field, good)
+    # one cache block of 2^32 bytes (2^20 KV heads x 16 x 128 x 2)
+    good = (a.num_kv_heads, a.num_q_heads)
+    a.num_kv_heads = a.num_q_heads = 1 << 20
+    assert lib.pa_prefill(ctypes.byref(a), None) == L.PA_E_UNSUPPORTED
+    a.num_kv_heads, a.num_q_heads = good
     a.num_seqs = 0
     assert lib.pa_prefill(ctypes.byref(a), None) == 0                      # nothing to do
 
