@@ -127,30 +127,42 @@ __device__ __forceinline__ void wait_and_meet() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// One ring load: 16 bytes from base + off (base the same for the whole wave,
-// off per lane) into LDS at lds + 16 * lane (lds, an LDS byte address, the
-// same for the whole wave), by global_load_lds_dwordx4 with a scalar base,
-// whose LDS address is M0 (saved and restored here).  It is issued from asm
-// so that the compiler, which cannot tell which stage a load targets, adds no
-// waits of its own for it in front of the LDS reads: the ring's waits are
-// explicit.  Hazards: the base is copied by a scalar move inside the asm, so
-// the load never reads a scalar register that a vector instruction (a
-// readfirstlane) wrote just before, and that move is also the one wait state
-// a load-to-LDS needs after the scalar write of M0.
-__device__ __forceinline__ void ring_load(const char* base, uint32_t off, uint32_t lds) {
-  // Both are the same in every lane; readfirstlane puts them in scalar
-  // registers.  It returns a signed int: each half is taken back through
-  // uint32_t, so the low half of the address is zero-extended, never
-  // sign-extended into the high half.
-  const uint32_t l = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
-  const uint64_t b = uint64_t(uintptr_t(base));
+// A wave-uniform 64-bit address in scalar registers.  readfirstlane returns
+// a signed int: each half is taken back through uint32_t, so the low half is
+// zero-extended, never sign-extended into the high half.
+__device__ __forceinline__ uint64_t sgpr64(const char* p) {
+  const uint64_t b = uint64_t(uintptr_t(p));
   const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b))));
   const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32))));
-  const uint64_t sb = (uint64_t(hi) << 32) | uint64_t(lo);
+  return (uint64_t(hi) << 32) | uint64_t(lo);
+}
+
+// The two ring loads of one piece: 16 bytes per lane from kb + off into LDS
+// at lds + 16 * lane, and from vb + off into LDS at lds + VOFF + 16 * lane
+// (kb, vb and lds, an LDS byte address, the same for the whole wave; off per
+// lane), by global_load_lds_dwordx4 with scalar bases, whose LDS address is
+// M0 (saved once and restored here).  They are issued from asm so that the
+// compiler, which cannot tell which stage a load targets, adds no waits of
+// its own for them in front of the LDS reads: the ring's waits are explicit.
+// Hazards: each base is copied by a scalar move inside the asm, so no load
+// reads a scalar register that a vector instruction (a readfirstlane) wrote
+// just before, and that move is also the one wait state a load-to-LDS needs
+// after the scalar write of M0.
+template <uint32_t VOFF>
+__device__ __forceinline__ void ring_load_kv(const char* kb, const char* vb, uint32_t off, uint32_t lds) {
+  const uint32_t l = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
+  const uint64_t ks = sgpr64(kb), vs = sgpr64(vb);
   uint32_t saved;
-  uint64_t copy;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_mov_b64 %1, %3\n\tglobal_load_lds_dwordx4 %2, %1\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved), "=&s"(copy) : "v"(off), "s"(sb), "s"(l) : "memory");
+  uint64_t kc, vc;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %6\n\t"
+               "s_mov_b64 %1, %4\n\t"
+               "global_load_lds_dwordx4 %3, %1\n\t"
+               "s_add_u32 m0, %6, %7\n\t"
+               "s_mov_b64 %2, %5\n\t"
+               "global_load_lds_dwordx4 %3, %2\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved), "=&s"(kc), "=&s"(vc) : "v"(off), "s"(ks), "s"(vs), "s"(l), "n"(VOFF) : "memory");
 }
 
 // float32 pair -> packed 16-bit pair, round to nearest even.
@@ -311,6 +323,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int last_blk = (ctx - 1) >> p.log2_block;
   const int last_row = (ctx - 1) & bmask;
   const int64_t head_off = int64_t(g) * p.tile_bytes;
+  const char* const kbase = p.k + head_off;
+  const char* const vbase = p.v + head_off;
   const uint32_t blk_stride = uint32_t(p.num_kv_heads) * uint32_t(p.tile_bytes);   // < 2^32 (checked on the host)
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) const char*)&lds[0][0][0]));
   // The block ids of a step are fetched (scalar loads) a pair of steps
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   auto fetch = [&](int step) {
 #pragma unroll
-    for (int c = 0; c < NDMA; ++c) ids[step & 1][c] = table[block_index(step, c)];
+    for (int c = 0; c < NDMA; ++c) ids[step & 1][c] = table[uint32_t(block_index(step, c))];
   };
   auto issue = [&](int step) {            // ids hold this step's block ids
 #pragma unroll
@@ -333,10 +347,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const int blk = min(max(ids[step & 1][c], 0), p.num_blocks - 1);
       const int cap = bidx == last_blk ? last_row : bmask;
       const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
-      const int64_t at = int64_t(uint64_t(uint32_t(blk)) * blk_stride) + head_off;
+      const uint64_t at = uint64_t(uint32_t(blk)) * blk_stride;
       const uint32_t dst = lds0 + uint32_t(step % kStages) * (2 * TILE) + uint32_t((c * kWaves + wv) * kWave * 16);
-      ring_load(p.k + at, off, dst);
-      ring_load(p.v + at, off, dst + TILE);
+      ring_load_kv<TILE>(kbase + at, vbase + at, off, dst);
     }
   };
 
