@@ -7,6 +7,8 @@ tolerance.  This must hold on consecutive calls, the second on a smaller
 batch.  That second call finds the first call's records still in the array,
 and must not read them.
 """
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -40,12 +42,21 @@ def test_static_decode_equals_pa_decode_on_consecutive_calls():
         for part in (0, 64):
             want = dev.decode(partition_size=part)
             got = torch.full_like(want, float("nan"))
+            # Tensors left by earlier tests must not be freed inside the measured
+            # window (a garbage collection there lowers the count): collect them
+            # first and hold the collector off until the count is read again.
+            gc.collect()
             torch.cuda.synchronize()
-            before = torch.cuda.memory_allocated()
-            P.pa_decode_static(got, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, wl.scale,
-                               partition_size=part)
-            torch.cuda.synchronize()
-            assert torch.cuda.memory_allocated() == before      # nothing allocated through torch
+            gc.disable()
+            try:
+                before = torch.cuda.memory_allocated()
+                P.pa_decode_static(got, dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, wl.scale,
+                                   partition_size=part)
+                torch.cuda.synchronize()
+                after = torch.cuda.memory_allocated()
+            finally:
+                gc.enable()
+            assert after == before      # nothing allocated through torch
             assert torch.equal(got, want), (wl.name, part)
             assert_close(got.cpu().numpy(), ref, wl.dtype, f"{wl.name} partition {part}")
 
