@@ -943,7 +943,8 @@ def bench_ceiling(dev, reps=20):
     """Read rates this GPU reaches with no arithmetic: a plain stream over
     1 GiB, and whole 4 KiB tiles at scattered indices of a 4 GiB buffer
     (the decode's (block, KV head) tile shape), 1 GiB read per launch; HIP
-    events around each launch."""
+    events around each launch.  Each with the default and with the
+    non-temporal cache policy (the one the decode uses for unshared rows)."""
     import ctypes
 
     import numpy as np
@@ -951,8 +952,10 @@ def bench_ceiling(dev, reps=20):
 
     import paged_kv_cache_147_amd as P
     lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_147_amd", "libpagedkv_ceiling.so"))
-    lib.pc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    lib.pc_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.pc_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
     stream = P.current_stream(dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     nbytes = 1 << 30
@@ -971,9 +974,10 @@ def bench_ceiling(dev, reps=20):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
-    def stream_read(i):
-        assert lib.pc_stream_read(bufs[i % 2].data_ptr(), nbytes, blocks, sink.data_ptr(), stream) == 0
+    def stream_read(i, nt=0):
+        assert lib.pc_stream_read(bufs[i % 2].data_ptr(), nbytes, blocks, sink.data_ptr(), nt, stream) == 0
     ms_stream = timed(stream_read)
+    ms_stream_nt = timed(lambda i: stream_read(i, 1))
     del bufs
     tile = 4096
     big = torch.ones(4 * nbytes, dtype=torch.uint8, device=dev)
@@ -983,9 +987,10 @@ def bench_ceiling(dev, reps=20):
     per_wave = 16
     tsink = torch.empty(-(-n_tiles // per_wave) * 64 * 16, dtype=torch.uint8, device=dev)
 
-    def tile_read(i):
-        assert lib.pc_tile_read(big.data_ptr(), ids[i % 2].data_ptr(), n_tiles, tsink.data_ptr(), stream) == 0
+    def tile_read(i, nt=0):
+        assert lib.pc_tile_read(big.data_ptr(), ids[i % 2].data_ptr(), n_tiles, tsink.data_ptr(), nt, stream) == 0
     ms_tile = timed(tile_read)
+    ms_tile_nt = timed(lambda i: tile_read(i, 1))
     del big
     torch.cuda.empty_cache()
     res = {"metric": "read rate with no arithmetic (context for the decode roofline)",
@@ -994,12 +999,18 @@ def bench_ceiling(dev, reps=20):
            "stream_read_frac": round(nbytes / (ms_stream * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
            "tile4k_read_gbps": round(nbytes / (ms_tile * 1e-3) / 1e9, 1),
            "tile4k_read_frac": round(nbytes / (ms_tile * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+           "stream_read_nt_gbps": round(nbytes / (ms_stream_nt * 1e-3) / 1e9, 1),
+           "stream_read_nt_frac": round(nbytes / (ms_stream_nt * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+           "tile4k_read_nt_gbps": round(nbytes / (ms_tile_nt * 1e-3) / 1e9, 1),
+           "tile4k_read_nt_frac": round(nbytes / (ms_tile_nt * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
            "config": {"stream": f"1 GiB, {blocks} workgroups of 256 threads, one 16-byte load per thread and "
                                 "iteration, 2 buffers alternated",
                       "tile4k": f"{n_tiles} 4 KiB tiles at random distinct indices of a 4 GiB buffer, {per_wave} "
                                 "tiles per 64-lane wave (4 in flight), 2 index sets alternated",
+                      "nt": "the _nt figures load with the non-temporal cache policy",
                       "timing": f"median of {reps} launches, HIP events"}}
-    log(f"[bench] ceiling: stream {res['stream_read_gbps']} GB/s, 4 KiB tiles {res['tile4k_read_gbps']} GB/s")
+    log(f"[bench] ceiling: stream {res['stream_read_gbps']} / {res['stream_read_nt_gbps']} (nt) GB/s, "
+        f"4 KiB tiles {res['tile4k_read_gbps']} / {res['tile4k_read_nt_gbps']} (nt) GB/s")
     return res
 
 
