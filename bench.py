@@ -10,7 +10,9 @@ several copies of the cache so no step finds the previous step's data in the
 caches.
 
 Prints ONE JSON line (rank 0, N = 1): value = logical KV bytes read per step
-/ step time (GB/s).  ``roofline`` is measured live with HIP events around
+/ step time (GB/s).  Before its W warmup steps each decode measurement runs
+untimed steps until the GPU's clocks have settled (``prewarm_steps``: at
+least 100 steps and 50 ms), so a short timed run reads the steady state.  ``roofline`` is measured live with HIP events around
 every pa_decode call in the timed region (partition + combine launches);
 beside its algorithmic ``frac`` it carries ``hbm_frac`` (the call's HBM bytes
 from the committed rocprofv3 counter summary, over the same time) and the
@@ -22,7 +24,8 @@ Nested objects in the same line:
                bytes), with its own roofline and oracle baseline;
   block_sweep  B = 8 / 16 / 32 at ctx 1000 x 128: paged, contiguous-layout
                and identity-placement pa_decode times and the overheads;
-  ceiling      plain streaming read and scattered 4 KiB-tile read rates;
+  ceiling      plain streaming read and scattered 4 KiB-tile read rates,
+               with the default and the non-temporal cache policy;
   prefill      pa_prefill on the Llama-3.1-8B-like prefill batch, TFLOP/s
                against the dense bf16 matrix-core peak;
   prefix_cache, swap, fp8   the prefix cache, the preemption copies, and the
@@ -48,6 +51,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak); sequences/sec"
 PEAK_HBM_GBPS = 8000.0
+# Untimed decode steps before the warmup steps (clock settling): at least this many, and
+# at least this long.
+PREWARM_STEPS = 100
+PREWARM_S = 0.05
 PREFILL_METRIC = "paged prefill attention: algorithmic TFLOP/s (% of MI355X dense bf16 matrix-core peak)"
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 WORKLOADS = {
@@ -772,14 +779,24 @@ def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_si
         if ev is not None:
             ev[1].record()
 
+    # Untimed pre-warm before the W warmup steps: the GPU's clocks take tens of
+    # milliseconds of load to settle, and a short timed run (the default
+    # --steps 20 --warmup 5 is ~5 ms of decode) would otherwise read part of
+    # that ramp.  At least PREWARM_STEPS steps and PREWARM_S seconds.
+    prewarm, t_w = 0, time.perf_counter()
+    while prewarm < PREWARM_STEPS or time.perf_counter() - t_w < PREWARM_S:
+        for _ in range(10):
+            step(prewarm)
+            prewarm += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
-        step(i)
+        step(prewarm + i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(prewarm + warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     dec_ms = [a.elapsed_time(b) for a, b in evs]
@@ -797,6 +814,7 @@ def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_si
         "unit": "GB/s",
         "steps": steps,
         "warmup": warmup,
+        "prewarm_steps": prewarm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
