@@ -644,13 +644,14 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode
         if ev is not None:
             ev[1].record()
 
+    prewarm = run_prewarm(step)   # untimed, as in bench_decode_step
     for i in range(warmup):
-        step(i)
+        step(prewarm + i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(prewarm + warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     dec_ms = [a.elapsed_time(b) for a, b in evs]
@@ -671,6 +672,7 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode
         "unit": "GB/s",
         "steps": steps,
         "warmup": warmup,
+        "prewarm_steps": prewarm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "dtype": "fp8_e4m3 codes, bf16 q, f32 accumulation",
@@ -736,6 +738,19 @@ def unique_kv_bytes(wl, tables, ctx):
     return n * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl.dtype)
 
 
+def run_prewarm(step):
+    """Untimed steps until the GPU's clocks have settled: at least PREWARM_STEPS
+    steps and PREWARM_S seconds.  Returns the number of steps run."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < PREWARM_STEPS or time.perf_counter() - t0 < PREWARM_S:
+        for _ in range(10):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_size=0, cpu=None):
     """One decode step (copies, pa_write_kv of the new tokens, pa_decode),
     timed over `steps` steps after `warmup`; every pa_decode call between HIP
@@ -782,13 +797,8 @@ def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_si
     # Untimed pre-warm before the W warmup steps: the GPU's clocks take tens of
     # milliseconds of load to settle, and a short timed run (the default
     # --steps 20 --warmup 5 is ~5 ms of decode) would otherwise read part of
-    # that ramp.  At least PREWARM_STEPS steps and PREWARM_S seconds.
-    prewarm, t_w = 0, time.perf_counter()
-    while prewarm < PREWARM_STEPS or time.perf_counter() - t_w < PREWARM_S:
-        for _ in range(10):
-            step(prewarm)
-            prewarm += 1
-        torch.cuda.synchronize()
+    # that ramp.
+    prewarm = run_prewarm(step)
     for i in range(warmup):
         step(prewarm + i)
     torch.cuda.synchronize()
