@@ -378,11 +378,14 @@ typedef struct pa_decode_args {
 /* Workspace bytes pa_decode needs for these arguments.  Validates the
  * arguments like pa_decode; needs no GPU.
  *
- * Fixed partitions: each partition's (max, sum, weighted sum), or 0 bytes
- * when every context fits one partition.  Balanced (-1): the schedule (per
- * sequence tile offsets, each piece's first sequence) and two (max, sum,
- * weighted sum) records per piece, sized for at most
- * min(8192, num_seqs * num_kv_heads * ceil(max_ctx / 16) / 8) pieces.  A
+ * One record per (sequence, query head, partition) of the longest context,
+ * or 0 bytes when every context fits one partition: the partition's max, sum
+ * of weights and a scale a (4 floats), and its head_dim weighted sums divided
+ * by a.  The sums are float32 for float32 caches; for 16-bit and E4M3 caches
+ * they are f16 under a power-of-two a chosen per record so that the record's
+ * largest magnitude lands in [2^14, 2^15) (relative rounding at most 2^-11 per
+ * value; the half-size records halve the lines the partition kernel writes,
+ * which measured 3.5% faster on the Llama-3.1-8B batch without sharing).  A
  * short launch after the decode kernel merges the records.  The contents need
  * no initialisation and are rewritten by each call, so one workspace serves
  * any number of calls ordered on one stream; two calls running at the same

@@ -27,7 +27,10 @@
 //     weights are never rounded to 16 bits);
 //   * when a context spans several partitions, each writes its (max, sum,
 //     weighted sum) to the workspace and decode_combine_kernel merges them
-//     with the log-sum-exp identity, in partition order.  (Merging inside the
+//     with the log-sum-exp identity, in partition order.  For 16-bit caches
+//     the weighted sums are stored as f16 under a power-of-two scale per row
+//     (record_scale_exp), half the lines of float32 records; float32 caches
+//     keep float32 records.  (Merging inside the
 //     same launch would need device-scope release/acquire fences per wave;
 //     on this GPU those write back and invalidate the XCD's L2 and cost far
 //     more than one short extra launch.)
@@ -497,12 +500,27 @@ void decode_kernel(DecodeParams p) {
       return;
     }
     const int64_t prow = rec0 + my_h * rec_stride;
+    float a = 1.f;  // the record's values times a are the weighted sums
+    if constexpr (T::bytes == 4) {
 #pragma unroll
-    for (int q = 0; q < PER; q += RUN) store_run<RUN>(p.part_o + prow * D + elem(q), acc + q, 1.f);
-    if (c == 0 && e0 == 0) {  // one lane per head
-      p.part_ml[prow * 2 + 0] = my_m;
-      p.part_ml[prow * 2 + 1] = my_l;
+      for (int q = 0; q < PER; q += RUN)
+        store_run<RUN>(reinterpret_cast<float*>(p.part_o) + prow * D + elem(q), acc + q, 1.f);
+    } else {
+      // The head's row of D sums sits in 64 / G consecutive lanes.
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+#pragma unroll
+      for (int mm = 1; mm < kWave / G; mm <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mm));
+      const int k = record_scale_exp(amax);
+      a = __builtin_ldexpf(1.f, -k);
+#pragma unroll
+      for (int q = 0; q < PER; q += RUN)
+        store_run<F16, RUN>(F16{}, reinterpret_cast<uint16_t*>(p.part_o) + prow * D + elem(q), acc + q,
+                            __builtin_ldexpf(1.f, k));
     }
+    if (c == 0 && e0 == 0)  // one lane per head
+      *reinterpret_cast<float4*>(p.part_ml + prow * 4) = make_float4(my_m, my_l, a, 0.f);
   };
 
   Unit unit;
@@ -562,7 +580,9 @@ void decode_kernel(DecodeParams p) {
 // Every load address is known up front: with at most 64 records (the usual
 // case) the (m, l) loads and the first 8 records' outputs are in flight
 // together, so the merge waits on memory about once after the context length.
-// Record i = partition i, row (head * num_parts + i).
+// Record i = partition i, row (head * num_parts + i): (m, l, a) and D values
+// whose products with a are the weighted sums (float32 values and a = 1 for
+// float32 caches, f16 values under a power-of-two a for the others).
 template <class T, int D>
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   const int64_t head = blockIdx.x;  // s * Hq + query head
@@ -576,8 +596,12 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   if (np <= 1) return;  // the partition kernel wrote this output itself
   const int64_t rec0 = head * p.num_parts;
   auto rec = [&](int i) -> int64_t { return rec0 + i; };
-  const float2* ml = reinterpret_cast<const float2*>(p.part_ml);
-  const float* po = p.part_o + lane * PER;
+  const float4* ml = reinterpret_cast<const float4*>(p.part_ml);
+  const int64_t po = lane * PER;  // this lane's first value in a record row
+  auto value = [&](int64_t r, int k) -> float {
+    if constexpr (T::bytes == 4) return reinterpret_cast<const float*>(p.part_o)[r * D + po + k];
+    else return widen1(F16{}, reinterpret_cast<const uint16_t*>(p.part_o)[r * D + po + k]);
+  };
 
   // Outputs are read kBatch records at a time, all loads of a batch issued
   // before any is used (an index past the round's last record re-reads that
@@ -590,7 +614,7 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
     for (int u = 0; u < kBatch; ++u) {
       const int64_t r = rec(base + min(i0 + u, n - 1));
 #pragma unroll
-      for (int k = 0; k < PER; ++k) x[u][k] = po[r * D + k];
+      for (int k = 0; k < PER; ++k) x[u][k] = value(r, k);
     }
   };
   float o[PER];
@@ -621,16 +645,16 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
   if (np <= kWave) {
     // One round: lane i holds record i's (m, l).  Its load and the first
     // batch's output loads go out together, ahead of the reductions.
-    const float2 mine = lane < np ? ml[rec(lane)] : make_float2(-INFINITY, 0.f);
+    const float4 mine = lane < np ? ml[rec(lane)] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
     load_batch(0, 0, np);
     __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
     const float M = wave_max(mine.x);
     const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past np
     L = mine.y * f;
-    add_batch(0, np, f);
+    add_batch(0, np, f * mine.z);
     for (int i0 = kBatch; i0 < np; i0 += kBatch) {
       load_batch(0, i0, np);
-      add_batch(i0, np, f);
+      add_batch(i0, np, f * mine.z);
     }
   } else {
     // Rounds of 64 records against the maximum over all of them.
@@ -639,12 +663,12 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeParams p) {
     M = wave_max(M);
     for (int base = 0; base < np; base += kWave) {
       const int n = min(np - base, kWave);
-      const float2 mine = lane < n ? ml[rec(base + lane)] : make_float2(-INFINITY, 0.f);
+      const float4 mine = lane < n ? ml[rec(base + lane)] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
       const float f = __builtin_amdgcn_exp2f(mine.x - M);  // 0 for lanes past n
       L += mine.y * f;
       for (int i0 = 0; i0 < n; i0 += kBatch) {
         load_batch(base, i0, n);
-        add_batch(i0, n, f);
+        add_batch(i0, n, f * mine.z);
       }
     }
   }
@@ -749,9 +773,11 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
     return fail(PA_E_UNSUPPORTED, "too many (partition, sequence, head) units for one launch");
   if (plan->num_parts > 1 && S > 0) {
     const size_t rows = size_t(S) * Hq * plan->num_parts;
+    // values: float32 for float32 caches, else f16; (m, l, a, unused) per row
+    const size_t value_bytes = kv == PA_F32 ? sizeof(float) : sizeof(uint16_t);
     plan->part_o_off = 0;
-    plan->part_ml_off = align256(rows * D * sizeof(float));
-    plan->workspace = plan->part_ml_off + align256(rows * 2 * sizeof(float));
+    plan->part_ml_off = align256(rows * D * value_bytes);
+    plan->workspace = plan->part_ml_off + align256(rows * 4 * sizeof(float));
   }
   return ok();
 }
@@ -759,7 +785,7 @@ pa_status plan_decode(int S, int Hq, int Hkv, int D, pa_dtype kv, pa_dtype out, 
 // Points the parameter block at the workspace regions of the plan.
 void bind_workspace(const Plan& plan, void* ws, DecodeParams* p) {
   char* base = static_cast<char*>(ws);
-  p->part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+  p->part_o = base + plan.part_o_off;
   p->part_ml = reinterpret_cast<float*>(base + plan.part_ml_off);
 }
 

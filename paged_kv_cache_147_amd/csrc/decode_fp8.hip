@@ -354,11 +354,25 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
   // Lane (m16, q4) holds head m16's columns NN (4 q4 + i) + nn in o[nn][i]:
   // NN consecutive values per i.
   const float l = fp8_sum_xor32(fp8_sum_xor16(run_l));
+  const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
+  const bool whole = nparts_seq == 1;  // the same for the whole wave
+  // A record's values are stored as f16 under a power-of-two scale
+  // (record_scale_exp) from the largest magnitude of the head's row, which
+  // its 4 lanes m16 + 16 q4 hold; every lane still takes part here.
+  int k = 0;
+  if (!whole) {
+    float amax = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[nn][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    k = record_scale_exp(amax * p.v_scale);
+  }
   if (m16 >= G) return;
   const int64_t row = head0 + m16;
-  const int nparts_seq = (ctx + p.part_tokens - 1) / p.part_tokens;
-  const bool whole = nparts_seq == 1;
-  const float f = whole ? p.v_scale / l : p.v_scale;
+  const float f = whole ? p.v_scale / l : p.v_scale * __builtin_ldexpf(1.f, k);
   const int64_t orow = whole ? row : row * p.num_parts + part;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -366,25 +380,25 @@ __global__ __launch_bounds__(kWave) void decode_fp8_kernel(DecodeParams p) {
     float y[NN];
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) y[nn] = o[nn][i] * f;
-    if (!whole || p.out_f32) {
-      float* of = (whole ? reinterpret_cast<float*>(p.out) : p.part_o) + d0;
+    if (whole && p.out_f32) {
+      float* of = reinterpret_cast<float*>(p.out) + d0;
 #pragma unroll
-      for (int k = 0; k < NN; k += 4) *reinterpret_cast<float4*>(of + k) = make_float4(y[k], y[k + 1], y[k + 2], y[k + 3]);
+      for (int kk = 0; kk < NN; kk += 4) *reinterpret_cast<float4*>(of + kk) = make_float4(y[kk], y[kk + 1], y[kk + 2], y[kk + 3]);
     } else {
+      // 16-bit output rows (q's type), or an f16 record row
       uint32_t w[NN / 2];
 #pragma unroll
-      for (int k = 0; k < NN / 2; ++k) w[k] = uint32_t(narrow(T{}, y[2 * k])) | (uint32_t(narrow(T{}, y[2 * k + 1])) << 16);
-      uint16_t* oh = reinterpret_cast<uint16_t*>(p.out) + d0;
+      for (int kk = 0; kk < NN / 2; ++kk) {
+        if (whole) w[kk] = uint32_t(narrow(T{}, y[2 * kk])) | (uint32_t(narrow(T{}, y[2 * kk + 1])) << 16);
+        else w[kk] = uint32_t(narrow(F16{}, y[2 * kk])) | (uint32_t(narrow(F16{}, y[2 * kk + 1])) << 16);
+      }
+      uint16_t* oh = reinterpret_cast<uint16_t*>(whole ? p.out : p.part_o) + d0;
       if constexpr (NN == 8) *reinterpret_cast<uint4*>(oh) = make_uint4(w[0], w[1], w[2], w[3]);
       else *reinterpret_cast<uint2*>(oh) = make_uint2(w[0], w[1]);
     }
   }
   if (whole) return;
-  const int64_t prow = orow;
-  if (q4 == 0) {
-    p.part_ml[prow * 2 + 0] = run_mc;
-    p.part_ml[prow * 2 + 1] = l;
-  }
+  if (q4 == 0) *reinterpret_cast<float4*>(p.part_ml + orow * 4) = make_float4(run_mc, l, __builtin_ldexpf(1.f, -k), 0.f);
 }
 
 template <class T, int D, int G>

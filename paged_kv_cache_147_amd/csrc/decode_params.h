@@ -17,8 +17,10 @@ struct DecodeParams {
   const char* v;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* part_o;        // [S][Hq][num_parts][D] unnormalised weighted sums of the partitions
-  float* part_ml;       // same rows, (max, sum of weights) in the log2 domain
+  void* part_o;         // [S][Hq][num_parts][D] the partitions' weighted sums, scaled (float32 for
+                        // float32 caches, f16 for the others; see record_scale_exp)
+  float* part_ml;       // same rows, (max in the log2 domain, sum of weights, a, unused): the weighted
+                        // sums are the stored values times a
   int64_t tile_bytes;   // paged: bytes of one (block, KV head) tile
   int64_t region_bytes; // contiguous: bytes of one (sequence, KV head) region
   int32_t num_seqs;
@@ -95,6 +97,19 @@ __device__ __forceinline__ int unit_of(int id, const DecodeParams& p, Unit* u, i
   }
   u->part = *ctx / p.part_tokens;
   return *ctx % p.part_tokens ? kUnitRange : kUnitNone;
+}
+
+// Power-of-two exponent k under which a record row whose largest magnitude is
+// amax is stored as f16: amax * 2^k lies in [2^14, 2^15), inside the f16
+// range, and every value keeps f16's 11 significant bits (the relative
+// rounding error is at most 2^-11; values below 2^-24 of the row maximum
+// round to subnormals or zero).  A zero or non-finite maximum gets k = 0.
+__device__ __forceinline__ int record_scale_exp(float amax) {
+  if (!(amax > 0.f) || !__builtin_isfinite(amax)) return 0;
+  // amax = m 2^e with m in [0.5, 1); k is kept within +-126 so that both 2^k
+  // and 2^-k are normal float32 numbers
+  const int k = 15 - __builtin_amdgcn_frexp_expf(amax);
+  return k < -126 ? -126 : (k > 126 ? 126 : k);
 }
 
 // Launches decode_fp8_kernel over the fixed-partition grid (E4M3 caches,

@@ -102,8 +102,12 @@ def test_decode_workspace_sizes():
     assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(partition_size=256)), ctypes.byref(n)) == 0
     rows = 4 * 32 * 4
     align = lambda x: (x + 255) // 256 * 256
-    # partials: o, then (m, l)
-    assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
+    # records: the f16 weighted sums (a bf16 cache), then (m, l, a, unused) float32
+    assert n.value == align(rows * 128 * 2) + align(rows * 4 * 4)
+    # a float32 cache keeps float32 sums
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(partition_size=256, kv_dtype=L.PA_F32)),
+                                         ctypes.byref(n)) == 0
+    assert n.value == align(rows * 128 * 4) + align(rows * 4 * 4)
     # a single partition needs no workspace
     assert lib.pa_decode_workspace_bytes(ctypes.byref(_args(max_ctx=256, partition_size=256)),
                                          ctypes.byref(n)) == 0
@@ -161,7 +165,7 @@ def test_automatic_partition_size(S, hkv, max_ctx, expect_parts):
     assert lib.pa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
     rows = S * 4 * hkv * expect_parts
     align = lambda x: (x + 255) // 256 * 256
-    assert n.value == align(rows * 128 * 4) + align(rows * 2 * 4)
+    assert n.value == align(rows * 128 * 2) + align(rows * 4 * 4)
 
 
 @pytest.mark.parametrize("part", [-1, -8, 4, 12])

@@ -157,12 +157,16 @@ F32_FLOOR = 2.5e-7   # float32 accumulation error of an O(1) output
 
 
 def p_round_floor(case, dtype):
-    """Error bound of an output from the probabilities' rounding: p.V takes P
-    rounded once to f16 whatever q's type, |dP| <= 2^-11 P, so an output -- a
-    convex combination of V rows -- is off by at most 2^-11 max|V|, plus the
+    """Error bound of an output from the kernel's two f16 roundings.  p.V takes
+    P rounded once to f16 whatever q's type, |dP| <= 2^-11 P, so an output -- a
+    convex combination of V rows -- is off by at most 2^-11 max|V|.  A context
+    of several partitions is merged from records whose weighted sums o_p are
+    stored in f16 under a power-of-two scale, each value within 2^-11 of
+    itself; the merge divides sum_p w_p o_p by sum_p w_p l_p with
+    |o_p| <= l_p max|V|, so that adds at most 2^-11 max|V| more.  Plus the
     float32 accumulation floor."""
     vmax = float(np.nanmax(np.abs(F.VALUES[case.vc[(case.vc & 0x7F) != 0x7F]]))) * case.v_scale
-    return 2.0 ** -11 * vmax + F32_FLOOR
+    return 2 * 2.0 ** -11 * vmax + F32_FLOOR
 
 
 def ulp(x, dtype):
