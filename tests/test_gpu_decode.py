@@ -114,6 +114,27 @@ def test_native_dtype_output_within_one_ulp(dtype):
         assert np.all(np.abs(got - ref_r) <= tol), part
 
 
+@pytest.mark.parametrize("shift", [100, -100])
+def test_records_keep_values_far_from_one(shift):
+    # The split-context records of a 16-bit cache hold f16 values under a
+    # power-of-two scale per row.  V rows scaled by 2^100 or 2^-100 (exact in
+    # bf16, far outside the f16 range) must merge like ordinary ones: no
+    # overflow to inf, no flush to zero, the usual error relative to the scale.
+    wl = W.independent(f"rec{shift}", [1500, 700, 1300, 40], (8, 2, 128, 16, "bf16"), 400, 128, seed=11)
+    v = wl.v_rows
+    before = to_f64(v.copy(), "bf16")
+    e = ((v >> 7) & 0xFF).astype(np.int32)
+    nz = e != 0
+    v[nz] = (v[nz] & 0x807F) | ((e[nz] + shift).astype(np.uint16) << 7)   # exponent field + shift
+    assert np.array_equal(to_f64(v, "bf16"), before * 2.0 ** shift)
+    dev = NativeDeviceRun(wl)
+    ref = oracle_out(wl)
+    for part in (0, 128):
+        got = dev.decode(partition_size=part).cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), part
+        assert_close(got / 2.0 ** shift, ref / 2.0 ** shift, "bf16", f"V scaled by 2^{shift}, partition {part}")
+
+
 def test_relabelling_sharing_and_repeat_are_bitwise_identical():
     mk = lambda share: W.shared_prefix("sp", 2, 4, 1008, [1, 7, 9, 300, 2, 5, 400, 12],
                                        (16, 4, 128, 16, "bf16"), 1024, 512, share=share, seed=8)
