@@ -209,6 +209,24 @@ def test_decode_shapes_against_oracle(dtype, d, G, B):
                            f"oracle {ref[bad][:4]} tol {tol[bad][:4]}")
 
 
+def test_records_keep_a_v_scale_far_from_one():
+    # The E4M3 kernel's split-context records are f16 under a power-of-two
+    # scale per row, taken after v_scale: V values near 2^60 (bf16 rows shifted
+    # by 2^60, quantised with v_scale = 2^60 V_SCALE) must come through the
+    # merge without overflow, within the usual error relative to the scale.
+    wl = W.independent("fp8_vscale", [1500, 700, 1300, 40], (8, 2, 128, 16, "bf16"), 400, 128, seed=12)
+    v = wl.v_rows
+    e = ((v >> 7) & 0xFF).astype(np.int32)
+    nz = e != 0
+    v[nz] = (v[nz] & 0x807F) | ((e[nz] + 60).astype(np.uint16) << 7)   # exponent field + 60
+    case = Fp8Case(wl, v_scale=2.0 ** 60 * V_SCALE)
+    ref = case.oracle()
+    for part in (0, 128):
+        got = case.decode(partition_size=part).cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), part
+        assert_close(got / 2.0 ** 60, ref / 2.0 ** 60, "bf16", f"v_scale 2^60, partition {part}")
+
+
 @pytest.mark.parametrize("name,make", [
     ("shared_prefix", lambda: W.shared_prefix("sp", 3, 4, 1008, [1, 7, 9, 16, 300, 2, 5, 8, 11, 3, 400, 12],
                                               (32, 8, 128, 16, "bf16"), 1024, 512, seed=8)),
