@@ -90,10 +90,16 @@ def decode_bytes(wl, ctx):
 
 
 def source_digest(names=("decode.hip", "decode_params.h", "device_common.h")):
+    """Digest of the kernel sources' code: comments, indentation and blank
+    lines are left out, so a comment edit does not retire a counter summary."""
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_147_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_147_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+        h.update(code.encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -478,8 +478,10 @@ void decode_kernel(DecodeParams p) {
   };
 
   // Finishes the partition: the group's normalised output rows when it is
-  // the whole context, else one (max, sum, weighted sum) record per head at
-  // rows rec0 + h * rec_stride of the workspace.
+  // the whole context, else one record per head at rows rec0 + h * rec_stride
+  // of the workspace: (max, sum, a) and the weighted sums divided by a (a = 1
+  // and float32 values for float32 caches; f16 values under a power-of-two a
+  // from record_scale_exp for 16-bit caches).
   auto finish = [&](bool whole, int64_t rec0, int64_t rec_stride) {
     refresh_lane();
     const float my_l = __shfl(run_l, my_h);  // lane h holds head h's max and sum
