@@ -194,6 +194,11 @@ struct PrefillParams {
   float scale_log2e;     // scale * log2(e): scores in the log2 domain
 };
 
+// A ring stage known at compile time, so that LDS addresses of a stage fold
+// into the instructions' offsets.
+template <int S>
+using Stage = std::integral_constant<int, S>;
+
 template <class T, int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int KK = D / 32;              // score MFMA steps over head_dim
@@ -336,19 +341,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // re-read rows of the last block (their scores are masked)
     return min(((step * kKeys) >> p.log2_block) + (((c * kWaves + wv) * RPI) >> p.log2_block), last_blk);
   };
-  auto fetch = [&](int step) {
+  auto fetch = [&](int step, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;   // step % kStages
 #pragma unroll
-    for (int c = 0; c < NDMA; ++c) ids[step & 1][c] = table[uint32_t(block_index(step, c))];
+    for (int c = 0; c < NDMA; ++c) ids[stage & 1][c] = table[uint32_t(block_index(step, c))];
   };
-  auto issue = [&](int step) {            // ids hold this step's block ids
+  auto issue = [&](int step, auto stage_c) {   // ids hold this step's block ids
+    constexpr int stage = decltype(stage_c)::value;   // step % kStages
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       const int bidx = block_index(step, c);
-      const int blk = min(max(ids[step & 1][c], 0), p.num_blocks - 1);
+      const int blk = min(max(ids[stage & 1][c], 0), p.num_blocks - 1);
       const int cap = bidx == last_blk ? last_row : bmask;
       const uint32_t off = uint32_t(min(lrow[c], cap) * ROW) + lbyte[c];
       const uint64_t at = uint64_t(uint32_t(blk)) * blk_stride;
-      const uint32_t dst = lds0 + uint32_t(step % kStages) * (2 * TILE) + uint32_t((c * kWaves + wv) * kWave * 16);
+      const uint32_t dst = lds0 + uint32_t(stage * 2 * TILE) + uint32_t((c * kWaves + wv) * kWave * 16);
       ring_load_kv<TILE>(kbase + at, vbase + at, off, dst);
     }
   };
@@ -356,8 +363,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // Step 0's ring loads go first; the query loads follow, and one wait the
   // compiler sees covers both, so that no wait for the queries is left for
   // it to place inside the loop (where it would drain the ring).
-  fetch(0);
-  issue(0);
+  fetch(0, Stage<0>{});
+  issue(0, Stage<0>{});
   // Queries: the B operand of S^T = K Q^T.  Lane (q4, m16) of tile j holds
   // elements [32 kk + 8 q4, +8) of row 16 j + m16 for step kk.
   u32x4_t qb[kSub][KK];
@@ -381,11 +388,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       for (int kk = 0; kk < KK; ++kk) qb[j][kk] ^= 0x80008000u;
   }
   if (1 < nsteps) {
-    fetch(1);
-    issue(1);
+    fetch(1, Stage<1>{});
+    issue(1, Stage<1>{});
   }
-  if (2 < nsteps) fetch(2);
-  if (3 < nsteps) fetch(3);
+  if (2 < nsteps) fetch(2, Stage<2>{});
+  if (3 < nsteps) fetch(3, Stage<3>{});
 
   // LDS read offsets.  K (A operand of S^T): lane (q4, m16) reads key row
   // m16 (+16 for the second tile), chunk 4 kk + q4.  V^T (transposing reads):
@@ -405,6 +412,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const float c = fmaxf(fabsf(p.scale_log2e), 1e-30f);
   const float slack = kSlack / c;         // kSlack in raw score units
   float run_m[kSub], run_mc[kSub];        // running max (raw), and times c
+  float run_top[kSub];                    // run_m + slack: a score above it moves the max
   // Running sums of the probabilities, from the matrix cores: one more block
   // of the p.V product with an all-ones V^T, so every element of run_l[j]
   // is row m16's sum of the very (rounded) P that went into O.
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   auto clear_state = [&]() {
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
-      run_m[j] = run_mc[j] = -INFINITY;
+      run_m[j] = run_mc[j] = run_top[j] = -INFINITY;
       run_l[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) o[j][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -421,12 +429,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
   clear_state();
 
-  auto compute = [&](int step, auto masked_step, auto split_step) {
+  auto compute = [&](int step, auto stage_c, auto masked_step, auto split_step, const u32x4_t& one) {
+    constexpr int stage = decltype(stage_c)::value;         // step % kStages
     constexpr bool masked = decltype(masked_step)::value;   // some row of the wave stops inside this step
     constexpr bool psplit = decltype(split_step)::value;    // bf16 V rows: P as two bf16 parts
     const int t0 = step * kKeys;
-    const char* kt = lds[step % kStages][0];
-    const char* vt = lds[step % kStages][1];
+    const char* kt = lds[stage][0];
+    const char* vt = lds[stage][1];
     // S^T tiles: element i of acc[j][h] is key t0 + 16 h + 4 q4 + i of row 16 j + m16.
     f32x4_t acc[kSub][2];
 #pragma unroll
@@ -455,11 +464,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       // The max moves only when some score of the wave's rows exceeds it by
       // more than kSlack in log2 units (always in the first step, where it
       // is -inf).
-      if (__builtin_amdgcn_ballot_w64(mx > run_m[j] + slack)) {
+      if (__builtin_amdgcn_ballot_w64(mx > run_top[j])) {
         const float mnew = fmaxf(run_m[j], max_xor32(max_xor16(mx)));
         const float f = __builtin_amdgcn_exp2f((run_m[j] - mnew) * c);
         run_m[j] = mnew;
         run_mc[j] = mnew * c;
+        run_top[j] = mnew + slack;
         run_l[j] *= f;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) o[j][nn] *= f;
@@ -501,15 +511,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         }
       }
     }
-    // the row sums: V^T replaced by ones (1.0 in the operand's type)
+    // the row sums: V^T replaced by ones
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
       if constexpr (psplit) {
-        const u32x4_t one = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
         run_l[j] = mfma(BF16{}, one, PH[j], run_l[j]);
         run_l[j] = mfma(BF16{}, one, PL[j], run_l[j]);
       } else {
-        const u32x4_t one = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
         run_l[j] = mfma(F16{}, one, PH[j], run_l[j]);
       }
     }
@@ -527,11 +535,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // elements of one row wherever the swizzle put it), so it needs only its
   // own wait for them, before the pair's barrier, and the barrier then
   // publishes the converted rows too.
-  auto convert_v = [&](int st) {
+  auto convert_v = [&](int st, auto stage_c) {
+    constexpr int s0 = decltype(stage_c)::value;      // st % kStages
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (st + h >= nsteps) break;
-      char* vt = lds[(st + h) % kStages][1];
+      char* vt = lds[s0 + h][1];
 #pragma unroll
       for (int cch = 0; cch < TILE / (kThreads * 16); ++cch) {
         u32x4_t* w = reinterpret_cast<u32x4_t*>(vt + (cch * kThreads + tid) * 16);
@@ -546,29 +555,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   };
 
   // All steps of the workgroup, pair by pair; for a bf16 cache in the first
-  // mode the V rows of each pair are turned into f16 first.
+  // mode the V rows of each pair are turned into f16 first.  The loop runs
+  // two pairs per turn, so that every stage index is a compile-time constant
+  // and LDS addresses take it as an instruction offset.  A pair's block ids
+  // for the pair after next are fetched once its steps are issued: a scalar
+  // load in flight would otherwise hold up the steps' first LDS reads (both
+  // count on the same wait counter).
   auto ring_loop = [&](auto split_mode) {
     constexpr bool psplit = decltype(split_mode)::value;
-    for (int st = 0; st < nsteps; st += 2) {
+    // the all-ones V^T of the row sums (1.0 in the operand's type), held in
+    // registers for the whole loop
+    u32x4_t one = psplit ? u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                         : u32x4_t{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+    asm volatile("" : "+v"(one));
+    auto one_step = [&](int s2, auto stage_c) {
+      if (s2 < nsteps && s2 * kKeys <= wave_last) {
+        if (s2 * kKeys + kKeys - 1 > wave_first) compute(s2, stage_c, std::true_type{}, split_mode, one);
+        else compute(s2, stage_c, std::false_type{}, split_mode, one);
+      }
+    };
+    // steps st and st + 1, held in stages S0 and S0 + 1
+    auto pair = [&](int st, auto stage_c) {
+      constexpr int S0 = decltype(stage_c)::value;
+      constexpr int S2 = (S0 + 2) % kStages;
       if constexpr (kConvV && !psplit) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's pieces of the pair
-        convert_v(st);
+        convert_v(st, stage_c);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       } else {
         wait_and_meet<0>();
       }
-      if (st + 2 < nsteps) issue(st + 2);
-      if (st + 3 < nsteps) issue(st + 3);
-      if (st + 4 < nsteps) fetch(st + 4);
-      if (st + 5 < nsteps) fetch(st + 5);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int s2 = st + h;
-        if (s2 < nsteps && s2 * kKeys <= wave_last) {
-          if (s2 * kKeys + kKeys - 1 > wave_first) compute(s2, std::true_type{}, split_mode);
-          else compute(s2, std::false_type{}, split_mode);
-        }
-      }
+      if (st + 2 < nsteps) issue(st + 2, Stage<S2>{});
+      if (st + 3 < nsteps) issue(st + 3, Stage<S2 + 1>{});
+      one_step(st, Stage<S0>{});
+      one_step(st + 1, Stage<S0 + 1>{});
+      if (st + 4 < nsteps) fetch(st + 4, Stage<S0>{});
+      if (st + 5 < nsteps) fetch(st + 5, Stage<S0 + 1>{});
+    };
+    for (int st = 0; st < nsteps; st += 4) {
+      pair(st, Stage<0>{});
+      if (st + 2 < nsteps) pair(st + 2, Stage<2>{});
     }
   };
 
@@ -592,14 +618,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (__builtin_amdgcn_readfirstlane(vflag)) {
       clear_state();
-      fetch(0);
-      issue(0);
+      fetch(0, Stage<0>{});
+      issue(0, Stage<0>{});
       if (1 < nsteps) {
-        fetch(1);
-        issue(1);
+        fetch(1, Stage<1>{});
+        issue(1, Stage<1>{});
       }
-      if (2 < nsteps) fetch(2);
-      if (3 < nsteps) fetch(3);
+      if (2 < nsteps) fetch(2, Stage<2>{});
+      if (3 < nsteps) fetch(3, Stage<3>{});
       ring_loop(std::true_type{});
     }
   } else {
