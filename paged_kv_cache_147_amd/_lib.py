@@ -453,13 +453,18 @@ def workspace_for(nbytes, device):
 
 
 def _workspace_on(nbytes, device, stream):
-    """A workspace made by torch's caching allocator on the current stream but
-    used on ``stream``: when that is another stream, the allocator is told, so
-    the memory is not handed out again before the work queued there has run."""
-    ws = workspace_for(nbytes, device)
+    """A workspace (its contents need no initialisation, so no kernel fills
+    it) made by torch's caching allocator on the current stream but used on
+    ``stream``.  When that is another stream, it first waits for the work
+    already queued on the current stream (the allocator may hand out memory
+    that work still uses), and the allocator is told, so the memory is not
+    handed out again before the work queued on ``stream`` has run."""
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     handle = (stream.value or 0) if stream is not None else None     # c_void_p(0).value is None
     if handle is not None and handle != torch.cuda.current_stream(device).cuda_stream:
-        ws.record_stream(torch.cuda.ExternalStream(handle, device=device))
+        other = torch.cuda.ExternalStream(handle, device=device)
+        other.wait_stream(torch.cuda.current_stream(device))
+        ws.record_stream(other)
     return ws
 
 

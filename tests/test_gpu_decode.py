@@ -331,8 +331,9 @@ except P.PagedKVError as e:
 
 def test_workspace_made_by_the_binding_on_any_stream():
     # with no workspace the binding allocates one; it must work on the default
-    # stream (handle 0) and on another stream (the allocator is told the
-    # memory is in use there)
+    # stream (handle 0) and on another stream (which first waits for the
+    # current stream's queued work, and the allocator is told the memory is in
+    # use there)
     wl = W.independent("ws_streams", [5, 700, 1300], (8, 2, 128, 16, "bf16"), 256, 96, seed=12)
     dev = NativeDeviceRun(wl)
     ref = oracle_out(wl)
