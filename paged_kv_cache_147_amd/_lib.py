@@ -567,8 +567,19 @@ def pa_decode_validate(q, k_cache, v_cache, block_tables, ctx_lens, max_ctx=0, s
         _dev(t)
     a = decode_args(None, q, k_cache, v_cache, block_tables, ctx_lens, 1.0, max_ctx, 0, None)
     count = torch.empty(1, dtype=torch.int32, device=q.device)
+    cur = torch.cuda.current_stream(q.device)
+    handle = (stream.value or 0) if stream is not None else None     # c_void_p(0).value is None
+    other = None
+    if handle is not None and handle != cur.cuda_stream:
+        # the count is allocated on the current stream: the other stream first
+        # waits for the work queued there, and the current stream waits for
+        # the check before the count is read back
+        other = torch.cuda.ExternalStream(handle, device=q.device)
+        other.wait_stream(cur)
     s = stream if stream is not None else current_stream(q.device)
     check(_lib.pa_decode_validate(ctypes.byref(a), count.data_ptr(), s), "pa_decode_validate")
+    if other is not None:
+        cur.wait_stream(other)
     return int(count.item())
 
 

@@ -300,6 +300,22 @@ def test_validate_counts_bad_tables_and_lengths():
     assert P.pa_decode_validate(dev.q, dev.k_cache, dev.v_cache, tables, ctx) == 2 + 1 + 30
 
 
+def test_validate_on_another_stream():
+    # the count is allocated on the current stream and filled on the caller's:
+    # the binding orders the two, so the count read back is the check's
+    wl = W.independent("val_stream", [5, 40, 300, 17], (8, 2, 64, 16, "f16"), 128, 32, seed=9)
+    dev = NativeDeviceRun(wl)
+    tables = dev.tables.clone()
+    tables[1, 0] = -5
+    tables[2, 18] = wl.num_blocks + 3
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        st = P.current_stream()
+    for _ in range(3):
+        assert P.pa_decode_validate(dev.q, dev.k_cache, dev.v_cache, tables, dev.ctx, stream=st) == 2
+        assert P.pa_decode_validate(dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.ctx, stream=st) == 0
+
+
 def test_debug_env_rejects_bad_tables_before_decoding():
     # PAGEDKV_DEBUG is read once per process: run the check in a child
     import os
