@@ -134,6 +134,45 @@ def test_prefill_bf16_values_beyond_the_f16_range():
     assert np.abs(ref[wide]).max() > 1000                 # the scaled rows did reach the outputs
 
 
+# contexts whose workgroups walk 1, 2, ..., 9 steps of 32 keys: the ring runs
+# its steps in pairs and two pairs per turn, so every remainder of the step
+# count (a lone last step, a lone last pair) is met
+TURN_PREFIX = [32 * k for k in range(9)]
+TURN_CHUNK = [8] * 9
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_every_ring_turn_length(dtype):
+    wl = W.prefill_chunks(f"pf_turns_{dtype}", TURN_PREFIX, TURN_CHUNK, (8, 2, 128, 16, dtype), 2 * 9 * 288 // 16,
+                          288 // 16, seed=21)
+    assert [(c - 1) // 32 + 1 for c in wl.info["ctx"]] == list(range(1, 10))
+    print(f"[prefill] {wl.name}", flush=True)
+    got = PrefillRun(wl).run().cpu().numpy()
+    assert_close(got, oracle_rows(wl), dtype, wl.name)
+
+
+def test_prefill_every_ring_turn_length_on_the_bf16_fallback():
+    # every V row of KV head 0 scaled by 2^17 (beyond the f16 range): each of
+    # its workgroups reruns its 1..9 steps on bf16 rows with P split, while
+    # KV head 1 stays on the f16 path
+    wl = W.prefill_chunks("pf_turns_wide", TURN_PREFIX, TURN_CHUNK, (8, 2, 128, 16, "bf16"), 2 * 9 * 288 // 16,
+                          288 // 16, seed=22)
+    v = wl.v_rows[:, 0]
+    exp = (v >> 7) & 0xFF
+    ok = (exp > 0) & (exp < 200)
+    v[ok] = v[ok] + np.uint16(17 << 7)                    # times 2^17, exactly
+    wl.v_rows[:, 0] = v
+    from oracle.bits import to_f64
+    big = np.abs(to_f64(wl.v_rows[:, 0], "bf16")).max()
+    assert big > 65504
+    got = PrefillRun(wl).run().cpu().numpy()
+    ref = oracle_rows(wl)
+    G = wl.num_q_heads // wl.num_kv_heads
+    assert_close(got[:, :G] / big, ref[:, :G] / big, "bf16", "KV head 0 (bf16 fallback)")
+    assert_close(got[:, G:], ref[:, G:], "bf16", "KV head 1 (f16 path)")
+    assert np.abs(ref[:, :G]).max() > 1000
+
+
 def test_prefill_one_row_chunks_match_decode():
     # one-token chunks are decode steps: pa_prefill and pa_decode agree
     wl = W.prefill_chunks("pf_dec", [5, 0, 70, 33, 400], [1] * 5, (32, 8, 128, 16, "bf16"), 256, 32, seed=3)
