@@ -12,8 +12,11 @@ caches.
 Prints ONE JSON line (rank 0, N = 1): value = logical KV bytes read per step
 / step time (GB/s).  Before its W warmup steps each decode measurement runs
 untimed steps until the GPU's clocks have settled (``prewarm_steps``: at
-least 100 steps and 50 ms), so a short timed run reads the steady state.  ``roofline`` is measured live with HIP events around
-every pa_decode call in the timed region (partition + combine launches);
+least 100 steps and 50 ms), so a short timed run reads the steady state.
+The K timed steps run with nothing else on the stream; ``roofline`` is then
+measured live with HIP events around every pa_decode call of K more steps
+(partition + combine launches; event records would add ~6.5 us to each
+step of the timed region, so they are kept out of it);
 beside its algorithmic ``frac`` it carries ``hbm_frac`` (the call's HBM bytes
 from the committed rocprofv3 counter summary, over the same time) and the
 rate of unique KV bytes.  ``cpu_baseline`` times the float64 oracle on every
@@ -271,8 +274,9 @@ def prefill_cpu_baseline(wl):
 
 
 def bench_prefill(wl, steps, warmup, dev, cpu=None):
-    """pa_prefill on the Llama-3.1-8B-like prefill batch: each launch timed
-    with HIP events on the stream it runs on."""
+    """pa_prefill on the Llama-3.1-8B-like prefill batch: `steps` launches
+    timed by the host clock, then `steps` more each between HIP events on the
+    stream it runs on (timed_passes)."""
     import numpy as np
     import torch
 
@@ -289,23 +293,17 @@ def bench_prefill(wl, steps, warmup, dev, cpu=None):
     stream = P.current_stream(dev)
     flops = prefill_flops(ctx, qs, wl.head_dim, wl.num_q_heads)
 
-    def call():
+    def call(i=0, ev=None):
+        if ev is not None:
+            ev[0].record()
         P.pa_prefill(out, q, run.k_cache, run.v_cache, run.tables, run.ctx, q_start, wl.scale, max_chunk,
                      stream=stream)
+        if ev is not None:
+            ev[1].record()
 
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t_start = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record()
-        call()
-        e1.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms = [a.elapsed_time(b) for a, b in evs]
-    ms_call = elapsed * 1e3 / steps
+    ms_call, ms = timed_passes(call, 0, steps)
     avg = float(np.mean(ms))
     log(f"[bench] prefill: {steps} launches, {ms_call:.4f} ms/call wall; kernel avg {avg:.4f} ms "
         f"(p10 {np.percentile(ms, 10):.4f}, p90 {np.percentile(ms, 90):.4f})")
@@ -653,15 +651,7 @@ def bench_fp8(wl, run, workload, dev, steps, warmup, nrep, cpu=None, bf16_decode
     prewarm = run_prewarm(step)   # untimed, as in bench_decode_step
     for i in range(warmup):
         step(prewarm + i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t_start = time.perf_counter()
-    for i in range(steps):
-        step(prewarm + warmup + i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = elapsed * 1e3 / steps
+    ms_step, dec_ms = timed_passes(step, prewarm + warmup, steps)
     dec_avg = float(np.mean(dec_ms))
     S, Hq = wl.num_seqs, wl.num_q_heads
     kv = int(sum(ctx)) * 2 * hkv * d
@@ -757,11 +747,34 @@ def run_prewarm(step):
     return n
 
 
+def timed_passes(step, first, steps):
+    """The timed region: `steps` steps with nothing else on the stream, timed
+    by the host clock between two synchronisations (ms per step).  Then the
+    same number of steps again with HIP events recorded around the measured
+    call of each (step(i, events)), which give the roofline's launch
+    durations.  The event records are kept out of the first pass: on this
+    stack two records per step add ~6.5 us to the step time while the
+    durations they measure are unchanged.  Returns (ms per step, per-call ms
+    from the events)."""
+    import torch
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(first + i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        step(first + steps + i, evs[i])
+    torch.cuda.synchronize()
+    return ms_step, [a.elapsed_time(b) for a, b in evs]
+
+
 def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_size=0, cpu=None):
     """One decode step (copies, pa_write_kv of the new tokens, pa_decode),
-    timed over `steps` steps after `warmup`; every pa_decode call between HIP
-    events on the stream it runs on.  Returns (result, device run, average
-    pa_decode ms)."""
+    timed over `steps` steps after `warmup`, then `steps` more with every
+    pa_decode call between HIP events on the stream it runs on
+    (timed_passes).  Returns (result, device run, average pa_decode ms)."""
     import numpy as np
     import torch
 
@@ -807,16 +820,7 @@ def bench_decode_step(wl, workload, desc, dev, steps, warmup, nrep, partition_si
     prewarm = run_prewarm(step)
     for i in range(warmup):
         step(prewarm + i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(steps):
-        step(prewarm + warmup + i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = elapsed * 1e3 / steps
+    ms_step, dec_ms = timed_passes(step, prewarm + warmup, steps)
     dec_avg = float(np.mean(dec_ms))
     log(f"[bench] {workload}: {steps} steps: {ms_step:.4f} ms/step; pa_decode avg {dec_avg:.4f} ms "
         f"(p10 {np.percentile(dec_ms, 10):.4f}, p90 {np.percentile(dec_ms, 90):.4f})")
