@@ -203,6 +203,24 @@ def test_edge_contexts():
     assert np.array_equal(one.reshape(2, 4, 128)[:, 0, :], vrow)
 
 
+def test_longest_contexts_and_widest_batch():
+    # contexts of 32768 and 16384 tokens (128 and 64 records per (sequence,
+    # head): the automatic choice here is 256-token partitions) next to a
+    # 3-token one; then 2048 short sequences (a wide grid of single-partition
+    # units)
+    wl = W.independent("long32k", [32768, 16384, 3], (32, 8, 128, 16, "bf16"), 3200, 2048, seed=31)
+    print(f"[decode] {wl.name}", flush=True)
+    dev = NativeDeviceRun(wl)
+    ref = oracle_out(wl)
+    assert_close(dev.decode().cpu().numpy(), ref, "bf16", wl.name)
+    assert_close(dev.decode(partition_size=128).cpu().numpy(), ref, "bf16", wl.name + " 128-token partitions")
+    ctx = np.random.default_rng(33).integers(1, 65, 2048)
+    wl = W.independent("wide2k", ctx.tolist(), (32, 8, 128, 16, "bf16"), 2048 * 4, 4, seed=34)
+    print(f"[decode] {wl.name}", flush=True)
+    dev = NativeDeviceRun(wl)
+    assert_close(dev.decode().cpu().numpy(), oracle_out(wl), "bf16", wl.name)
+
+
 def test_zero_and_negative_context_give_zero_rows():
     wl = W.independent("z", [5, 40], (8, 2, 64, 16, "f16"), 64, 8, seed=1)
     dev = NativeDeviceRun(wl)
