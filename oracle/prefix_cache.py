@@ -34,10 +34,10 @@ The model, written from that description:
 * With the cache on, a released sequence gives back its blocks last to
   first, so a block's descendants are released (and evicted) before it.
 
-Readings where the pages are silent (each also stated in the design doc's reading
-table): the eviction order is least-recently-released; an admission's hit
-may cover the whole prompt; plain admission and growth without token ids
-leave the sequence's later blocks unregistered.
+Readings where the pages are silent: the eviction order is
+least-recently-released; an admission's hit may cover the whole prompt;
+plain admission and growth without token ids leave the sequence's later
+blocks unregistered.
 """
 from .pool_model import BlockPoolModel, PoolError
 
